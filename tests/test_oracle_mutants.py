@@ -1,0 +1,72 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check that
+at least one pin catches each of them.  The copies live in a temporary
+directory; the real oracle is untouched."""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+from oracle import build as oracle_build
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "vpa_ref.c")
+
+# (name, exact text in vpa_ref.c, replacement)
+MUTANTS = [
+    ("tie_goes_to_highest_id",
+     "    if (a == b)\n        return ia < ib;", "    if (a == b)\n        return ia > ib;"),
+    ("nan_loses",
+     "    if (a_nan)\n        return 1;", "    if (a_nan)\n        return 0;"),
+    ("nan_tie_highest_id",
+     "    if (a_nan && b_nan)\n        return ia < ib;", "    if (a_nan && b_nan)\n        return ia > ib;"),
+    ("signed_zeros_differ",
+     "    if (a == b)\n        return ia < ib;",
+     "    if (a == b && signbit(a) != signbit(b))\n        return signbit(b) != 0;\n"
+     "    if (a == b)\n        return ia < ib;"),
+    ("subnormals_flushed",
+     "    return (double)f;", "    return fpclassify(f) == FP_SUBNORMAL ? 0.0 : (double)f;"),
+    ("bf16_not_widened",
+     "        return (uint32_t)h << 16;", "        return (uint32_t)h << 15;"),
+    ("padding_not_masked_in_argmax",
+     "        for (int64_t c = 1; c < vocab; ++c) {", "        for (int64_t c = 1; c < ld; ++c) {"),
+    ("padding_not_masked_in_stats",
+     "                if (hi > vocab)\n                    hi = vocab;", ""),
+    ("shard_local_blocks",
+     "                int64_t b = shard_lo / block + j;\n                int64_t lo = b * block, hi = lo + block;",
+     "                int64_t lo = shard_lo + (int64_t)j * block, hi = lo + block;"),
+    ("slot_count_short",
+     "        if (last - first + 1 > m)\n            m = last - first + 1;",
+     "        if (last - first > m)\n            m = last - first;"),
+    ("combine_by_value_only",
+     "            if (ref_better(ref_value(st.val_bits), st.id, ref_value(best.val_bits), best.id))\n                best = st;\n        }\n    return best;",
+     "            if (ref_value(st.val_bits) > ref_value(best.val_bits))\n                best = st;\n        }\n    return best;"),
+    ("accept_counts_all_matches",
+     "    while (n < k && draft[n] == target[n])\n        ++n;",
+     "    for (int32_t q = 0; q < k; ++q)\n        n += draft[q] == target[q];"),
+    ("correction_is_draft",
+     "        out[j] = j < n ? draft[j] : (j == n ? target[j] : -1);",
+     "        out[j] = j < n ? draft[j] : (j == n ? (j < k ? draft[j] : target[j]) : -1);"),
+    ("rejected_off_by_one",
+     "    *n_rejected = k - n;", "    *n_rejected = k - n + 1;"),
+    ("bonus_from_last_draft_row",
+     "        tgt[k] = ref_combine_row(bonus_stats, n_shards, n_req, r, m_bonus).id;",
+     "        tgt[k] = tgt[k - 1];"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mutant_src = tmp_path / "vpa_ref_mutant.c"
+    mutant_src.write_text(src.replace(old, new))
+    lib = oracle_build.build(src=str(mutant_src), lib=str(tmp_path / "libmutant.so"),
+                               strict=False)
+    runner = os.path.join(os.path.dirname(os.path.abspath(__file__)), "pin_runner.py")
+    res = subprocess.run([sys.executable, runner, lib], capture_output=True, text=True, timeout=600)
+    caught = [ln.split()[1] for ln in res.stdout.splitlines() if ln.startswith("caught")]
+    crashed = res.returncode != 0
+    assert caught or crashed, f"no pin catches the mutant {name}:\n{res.stdout}{res.stderr[-2000:]}"
+    shutil.rmtree(tmp_path, ignore_errors=True)
