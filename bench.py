@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Throughput of the vocab-parallel greedy argmax + greedy verification path
+on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic logits
+shaped like the 4096-row stress workload (vocabulary 200064, bf16 ~N(0,3),
+8 logical vocabulary shards):
+  * draft side: fused get_top_tokens (vpa_top_tokens, 8192-column blocks) over
+    4096 rows of draft-model logits -- padding mask, per-block statistics in
+    rank order, combination into the global argmax;
+  * target side: greedy verification of 682 requests x (K=5 drafts + 1 bonus)
+    = 4092 rows of target-model logits -- per-block statistics (8192 columns
+    for draft rows, 1024 for bonus rows, one launch, vpa_verify_stats) and the
+    finishing kernel (vpa_greedy_verify).
+Draft and target logits are two distinct 1.6 GB buffers resident in HBM, so
+no pass re-reads the other's data from cache.  Drafts copy the target token
+with probability 0.4, else a uniform draw (the target tokens come from an
+untimed call before timing).
+
+Prints one JSON line: value = logits rows reduced per second (4096 + 4092
+rows per step); roofline = the block-statistics kernel (the verification
+statistics launch, timed by HIP events on the launch stream) against MI355X's
+8 TB/s HBM peak; cpu_baseline = the CPU oracle timed on this host on the
+same step.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "logits rows/s + achieved HBM GB/s (% peak), V=200064 bf16 argmax+verify"
+PEAK_HBM_GBPS = 8000.0
+V, W, S = 200064, 25008, 8
+N_ROWS, K = 4096, 5
+R = N_ROWS // (K + 1)                       # 682 requests; rows 4092..4095 are not referenced
+B_DRAFT, B_BONUS = 8192, 1024
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_stats_bf16_v200064_traffic.json")
+KERNEL_SOURCES = ("vocab_argmax_amd/csrc/block_stats.hip", "vocab_argmax_amd/csrc/vpa_device.h")
+
+
+def slots(w, s, b):
+    return max((i * w + w - 1) // b - (i * w) // b + 1 for i in range(s))
+
+
+def algorithmic_bytes():
+    """Bytes the method must move, per call (valid logits columns only)."""
+    e = 2
+    m_tt, m_d, m_b = slots(W, S, B_DRAFT), slots(W, S, B_DRAFT), slots(W, S, B_BONUS)
+    top_tokens = N_ROWS * (V * e + S * m_tt * 8 * 2 + 8)          # logits + stats w/r + id/value
+    verify_stats = R * K * (V * e + S * m_d * 8) + R * (V * e + S * m_b * 8)
+    greedy = R * (K * S * m_d * 8 + S * m_b * 8 + 4 * K + 4 * (K + 1) * 2 + 8)
+    return {"top_tokens": top_tokens, "verify_stats": verify_stats, "greedy_verify": greedy}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per verification-statistics launch from the committed PMC
+    summary, only if it was taken on the kernel source as it is now."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(draft_cpu, target_cpu, drafts_cpu, gpu_out, min_seconds=10.0, max_reps=5):
+    """The CPU oracle on the same step, single-threaded, pinned to one core."""
+    import oracle
+    import torch
+    try:
+        os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
+    except (AttributeError, OSError):
+        pass
+    draft_rows, bonus_rows = oracle.verify_rows(R, K)
+    reps, elapsed, result = 0, 0.0, None
+    while reps < max_reps and (elapsed < min_seconds or reps == 0):
+        t0 = time.perf_counter()
+        ids, vals = oracle.argmax(draft_cpu, V)
+        dst = oracle.block_stats(target_cpu, V, W, S, B_DRAFT, rows=draft_rows)
+        bst = oracle.block_stats(target_cpu, V, W, S, B_BONUS, rows=bonus_rows)
+        ver = oracle.greedy_verify(dst, bst, drafts_cpu)
+        elapsed += time.perf_counter() - t0
+        reps += 1
+        result = (ids, vals, ver)
+    ids, vals, ver = result
+    g_ids, g_vals, g_out, g_ns, g_nr = gpu_out
+    parity = (torch.equal(ids, g_ids) and torch.equal(vals, g_vals.to(torch.int64) & 0xFFFFFFFF)
+              and torch.equal(ver[0], g_out) and torch.equal(ver[1], g_ns)
+              and torch.equal(ver[2], g_nr))
+    rows = reps * (N_ROWS + R * (K + 1))
+    return {"value": rows / elapsed, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} full step(s): {N_ROWS} argmax rows + {R * (K + 1)} verification "
+                      f"rows of the same workload, {elapsed:.1f} s, one thread pinned to one core"
+                      f" of {os.cpu_count()}",
+            "parity_with_gpu_step": bool(parity)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the vocabulary shards are logical); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import vocab_argmax_amd as vpa
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating 2 x {N_ROWS} x {V} bf16 logits on {torch.cuda.get_device_name(dev)}",
+          file=sys.stderr, flush=True)
+    draft_w = workloads.config4(device=dev, n_rows=N_ROWS, seed=1004)
+    target_w = workloads.config4(device=dev, n_rows=N_ROWS, seed=2004)
+    xd, xt = draft_w.logits, target_w.logits
+
+    # untimed: target tokens -> draft ids that copy them with p = 0.4
+    tgt_ids, _ = vpa.top_tokens(xt, V, W, S, B_DRAFT)
+    drafts_cpu = workloads.compose_drafts(tgt_ids[:R * (K + 1)].reshape(R, K + 1).cpu(),
+                                          target_w.draft_plan, target_w.draft_uniform)
+    drafts = drafts_cpu.to(dev)
+
+    ws = torch.empty(vpa.top_tokens_workspace(V, W, S, N_ROWS, B_DRAFT), dtype=torch.uint8,
+                     device=dev)
+    ids = torch.empty(N_ROWS, dtype=torch.int32, device=dev)
+    vals = torch.empty(N_ROWS, dtype=torch.int32, device=dev)
+    md, mb = vpa.stats_slots(W, S, B_DRAFT), vpa.stats_slots(W, S, B_BONUS)
+    dst = torch.empty((S, R * K, md, 2), dtype=torch.int32, device=dev)
+    bst = torch.empty((S, R, mb, 2), dtype=torch.int32, device=dev)
+    out = torch.empty((R, K + 1), dtype=torch.int32, device=dev)
+    ns = torch.empty(R, dtype=torch.int32, device=dev)
+    nr = torch.empty(R, dtype=torch.int32, device=dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        vpa.top_tokens(xd, V, W, S, B_DRAFT, workspace=ws, ids=ids, val_bits=vals)
+        if ev:
+            ev[1].record()
+        vpa.verify_stats(xt, V, W, S, R, K, B_DRAFT, B_BONUS, out=(dst, bst))
+        if ev:
+            ev[2].record()
+        vpa.greedy_verify(dst, bst, drafts, with_targets=False, out=(out, ns, nr, None))
+        if ev:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_step = wall * 1e3 / args.steps
+    tt_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    vs_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    gv_ms = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+    alg = algorithmic_bytes()
+    step_bytes = sum(alg.values())
+    rows_per_step = N_ROWS + R * (K + 1)
+    achieved = alg["verify_stats"] / (vs_ms * 1e-3) / 1e9
+    traffic = measured_traffic()
+
+    result = {
+        "metric": METRIC,
+        "value": rows_per_step / (ms_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"stress_v{V}_bf16_s{S}: top_tokens {N_ROWS} rows (B={B_DRAFT}) + greedy "
+                         f"verification {R} req x (K={K}+1) rows (B={B_DRAFT}/{B_BONUS})"),
+            "vocab": V, "shard_width": W, "n_shards": S, "rows_top_tokens": N_ROWS,
+            "rows_verify": R * (K + 1), "k": K, "device": torch.cuda.get_device_name(dev),
+        },
+        "gbps_step": step_bytes / (ms_step * 1e-3) / 1e9,
+        "hbm_frac_step": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "phase_ms": {"top_tokens": tt_ms, "verify_stats": vs_ms, "greedy_verify": gv_ms},
+        "top_tokens_gbps": alg["top_tokens"] / (tt_ms * 1e-3) / 1e9,
+        "roofline": {
+            "kernel": "block_stats_kernel<bf16> (vpa_verify_stats launch)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": alg["verify_stats"],
+            "avg_launch_us": vs_ms * 1e3,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        torch.cuda.synchronize()
+        gpu_out = (ids.cpu(), vals.cpu(), out.cpu(), ns.cpu(), nr.cpu())
+        result["cpu_baseline"] = cpu_baseline(xd.cpu(), xt[:R * (K + 1)].cpu(), drafts_cpu,
+                                              gpu_out)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,190 @@
+/*
+ * vpa.h -- C ABI of the vocab-parallel greedy argmax library for MI355X
+ * (gfx950).
+ *
+ * The library computes, on one GPU, the hot path of greedy speculative
+ * decoding with a vocabulary-sharded LM head, as the vLLM pages describe it:
+ *
+ *  - vLLM PR #34049 "[Spec Decode] Reduce TP communication for speculative
+ *    decoding draft token generation", section "Solution": each tensor-
+ *    parallel rank takes the argmax of its own vocabulary shard, the ranks
+ *    exchange only (max value, global index) pairs, and a final reduction
+ *    over the ranks yields the global argmax.
+ *  - vLLM PR #62604 (sharded greedy verification and fused get_top_tokens),
+ *    section "Purpose": item 1 -- every rank reduces its shard to per-block
+ *    (max, token id) statistics with the global block boundaries of the full
+ *    vocabulary (8192 columns for draft positions, 1024 for the bonus
+ *    position), kept across shard edges; after the statistics are gathered,
+ *    one step finishes the global argmax, the acceptance, the bonus token and
+ *    the sampled/rejected counts; vocabularies below 2^24.  Item 2 -- the
+ *    fused get_top_tokens masks the vocabulary padding and picks the same
+ *    token as torch.argmax: the lowest id on ties, and NaN above every
+ *    number.  Section "Test Plan" -- shard statistics are laid out in rank
+ *    order, as a dim-0 all-gather produces them.
+ *
+ * Vocabulary shards here are logical: shard s of S holds global columns
+ * [s*W, (s+1)*W) of the padded vocabulary (S*W >= V); columns [V, S*W) are
+ * padding and are never read.  Statistics of all local shards are written in
+ * rank order into one device buffer, the layout a dim-0 all-gather of the
+ * per-rank statistics would produce, so a multi-GPU caller can gather them
+ * with one collective and run the combining calls unchanged.
+ *
+ * Conventions shared by every call:
+ *  - Pointers named logits, stats, ids, val_bits, draft_ids, out_tokens,
+ *    num_sampled, num_rejected, target_ids, rows and workspace are DEVICE
+ *    memory owned by the caller.  The library never allocates or frees.
+ *  - Every call only enqueues work on `stream` (a hipStream_t passed as
+ *    void*; NULL is the default stream) and returns without synchronising;
+ *    outputs are defined once the stream reaches that point.
+ *  - Arguments are validated on the host before any HIP call.  On
+ *    VPA_ERR_INVALID or VPA_ERR_UNSUPPORTED nothing has been enqueued and
+ *    vpa_last_error() describes the problem.  VPA_ERR_HIP reports a failed
+ *    launch; launches of the same call that precede it may have been
+ *    enqueued.
+ *  - A call with zero rows (or zero requests) returns VPA_OK and enqueues
+ *    nothing.
+ *  - Logits are row-major: element (row, c) of the local columns sits at
+ *    logits[row*ld + c], c counted from the first local shard.  The pointer
+ *    must be aligned to the element size; rows may start at any such address.
+ *  - Value bits are the fp32 bit pattern of the chosen element (a bf16
+ *    pattern h widens to h<<16), NaN payload and the sign of zero kept.
+ *  - Results are deterministic: the same inputs give bitwise identical
+ *    outputs on every run, whatever the launch shape.
+ *  - The library is greedy-only: it assumes the caller has already applied
+ *    any positive logit scale and routes sampled requests elsewhere.
+ */
+#ifndef VPA_H
+#define VPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    VPA_OK = 0,
+    VPA_ERR_INVALID = 1,     /* bad size, geometry, alignment or null pointer */
+    VPA_ERR_UNSUPPORTED = 2, /* a dtype the library does not handle */
+    VPA_ERR_HIP = 3          /* the HIP runtime refused a launch */
+} vpa_status;
+
+typedef enum { VPA_F32 = 0, VPA_BF16 = 1 } vpa_dtype;
+
+/* One (max, token id) statistic, 8 bytes.  An empty slot holds
+ * {VPA_EMPTY_BITS, VPA_EMPTY_ID}: -inf with an id above every token, so it
+ * loses to every real statistic, -inf included. */
+typedef struct {
+    uint32_t val_bits; /* fp32 bit pattern of the block's winning value */
+    int32_t id;        /* global token id of the winner */
+} vpa_stat;
+
+#define VPA_EMPTY_BITS 0xFF800000u
+#define VPA_EMPTY_ID 0x7FFFFFFF
+#define VPA_MAX_VOCAB (1 << 24) /* the vocabulary must stay below this */
+
+/* Vocabulary geometry: V valid columns, S shards of W columns each. */
+typedef struct {
+    int64_t vocab;       /* V, 1 <= V < 2^24 */
+    int64_t shard_width; /* W >= 1 */
+    int32_t n_shards;    /* S >= 1, S*W >= V (a shard may hold only padding) */
+} vpa_vocab;
+
+/* Statistic slots per shard, M: the largest number of global blocks
+ * [b*block, (b+1)*block) that any shard [s*W, (s+1)*W), s < S, touches
+ * (PR #62604, "Purpose" item 1: global block boundaries across shard edges).
+ * Slot j of shard s is block floor(s*W/block)+j cut to the shard and to
+ * [0, V).  Returns -1 on invalid arguments (W < 1, S < 1, block < 1). */
+int32_t vpa_stats_slots(int64_t shard_width, int32_t n_shards, int32_t block);
+
+/* Per-block statistics of the local shards (PR #62604, "Purpose" item 1;
+ * the per-rank step of PR #34049, "Solution").
+ *  logits   [*, ld] of dtype `dtype`; column 0 is global column first_shard*W.
+ *           Row stride ld must cover the valid local columns:
+ *           ld >= min(n_local_shards*W, V - first_shard*W).
+ *  first_shard, n_local_shards  the shard range this call reduces
+ *           (0 <= first_shard, first_shard + n_local_shards <= S).  A rank of
+ *           a multi-GPU job passes its own rank and 1; one GPU holding every
+ *           shard passes 0 and S.
+ *  rows     n_rows int32 row indices into logits, or NULL for 0..n_rows-1.
+ *           An index outside [0, logits_rows) yields empty statistics for
+ *           that row and reads nothing.
+ *  logits_rows  number of rows the logits buffer holds (bounds rows[]).
+ *  block    global block size (>= 1).
+ *  stats    out, [n_local_shards][n_rows][M] with M = vpa_stats_slots(W,S,block),
+ *           8-byte aligned.  Slot i of shard s describes row rows[i]. */
+vpa_status vpa_block_stats(const void* logits, vpa_dtype dtype, int64_t ld, vpa_vocab v,
+                           int32_t first_shard, int32_t n_local_shards, const int32_t* rows,
+                           int64_t n_rows, int64_t logits_rows, int32_t block, vpa_stat* stats,
+                           void* stream);
+
+/* Both statistics of a greedy verification batch in one launch (PR #62604,
+ * "Purpose" item 1: draft positions use 8192-column blocks, the bonus
+ * position 1024-column blocks).  Request r owns logits rows
+ * r*(K+1) .. r*(K+1)+K: K draft positions, then the bonus position; the
+ * logits buffer must hold at least n_req*(K+1) rows.
+ *  draft_stats  out, [n_local_shards][n_req*K][M_draft], row r*K+j is draft
+ *               position j of request r; M_draft = vpa_stats_slots(W,S,block_draft).
+ *  bonus_stats  out, [n_local_shards][n_req][M_bonus]; M_bonus likewise.
+ * Other arguments as vpa_block_stats; k >= 1. */
+vpa_status vpa_verify_stats(const void* logits, vpa_dtype dtype, int64_t ld, vpa_vocab v,
+                            int32_t first_shard, int32_t n_local_shards, int64_t n_req, int32_t k,
+                            int32_t block_draft, int32_t block_bonus, vpa_stat* draft_stats,
+                            vpa_stat* bonus_stats, void* stream);
+
+/* Rank-order combination of gathered statistics into the global argmax
+ * (PR #34049, "Solution", step 3).
+ *  stats    [n_shards][n_rows][m], e.g. the concatenation of every rank's
+ *           vpa_block_stats output (n_shards = S, all shards present).
+ *  ids      out, int32 [n_rows]: the global argmax of each row.
+ *  val_bits out, uint32 [n_rows], or NULL: the fp32 bits of the maximum. */
+vpa_status vpa_combine_stats(const vpa_stat* stats, int32_t n_shards, int64_t n_rows, int32_t m,
+                             int32_t* ids, uint32_t* val_bits, void* stream);
+
+/* Workspace bytes vpa_top_tokens needs for n_rows rows (0 if the arguments
+ * are invalid or n_rows is 0). */
+size_t vpa_top_tokens_workspace(vpa_vocab v, int64_t n_rows, int32_t block);
+
+/* Fused draft-side get_top_tokens over every shard of a row (PR #62604,
+ * "Purpose" item 2): padding mask, per-block statistics of all S shards in
+ * rank order (kept in `workspace`, [S][n_rows][M]), and their combination
+ * into the global argmax.
+ *  logits     [n_rows, ld] holding all S shards side by side (global column
+ *             c at logits[row*ld + c]); ld >= V.
+ *  workspace  device memory of at least vpa_top_tokens_workspace() bytes,
+ *             8-byte aligned; its contents on entry do not matter.
+ *  ids, val_bits  as vpa_combine_stats (val_bits may be NULL). */
+vpa_status vpa_top_tokens(const void* logits, vpa_dtype dtype, int64_t ld, vpa_vocab v,
+                          int64_t n_rows, int32_t block, void* workspace, size_t workspace_bytes,
+                          int32_t* ids, uint32_t* val_bits, void* stream);
+
+/* Greedy verification from gathered statistics (PR #62604, "Purpose" item 1
+ * and "Test Plan"): the target token of each position is the combined
+ * argmax of its row; drafts are accepted while they equal their target;
+ * the first differing position -- or position K when all K match -- emits
+ * its target token (correction or bonus token); later positions hold -1.
+ *  draft_stats  [n_shards][n_req*K][m_draft], bonus_stats [n_shards][n_req][m_bonus]
+ *               (the layout vpa_verify_stats writes).
+ *  draft_ids    int32 [n_req][K]; any value is legal, -1 marks a placeholder,
+ *               and only a value equal to the target token is accepted.
+ *  out_tokens   out, int32 [n_req][K+1].
+ *  num_sampled  out, int32 [n_req]: accepted + 1.
+ *  num_rejected out, int32 [n_req]: K - accepted.
+ *  target_ids   out, int32 [n_req][K+1], or NULL: the target token of every
+ *               position. */
+vpa_status vpa_greedy_verify(const vpa_stat* draft_stats, int32_t m_draft,
+                             const vpa_stat* bonus_stats, int32_t m_bonus, int32_t n_shards,
+                             int64_t n_req, int32_t k, const int32_t* draft_ids,
+                             int32_t* out_tokens, int32_t* num_sampled, int32_t* num_rejected,
+                             int32_t* target_ids, void* stream);
+
+/* Message describing the last non-OK status returned on the calling thread
+ * ("" if none).  The pointer stays valid until the next call on that thread. */
+const char* vpa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VPA_H */

@@ -1,0 +1,161 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the header
+declares, and rejects invalid arguments before any HIP call (so these calls
+need no GPU; pointers passed here are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bruteforce as bf
+import vocab_argmax_amd as vpa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "vpa.h")
+FAKE = ctypes.c_void_p(0x10000)     # aligned, never dereferenced by a rejected call
+FAKE_ODD = ctypes.c_void_p(0x10001)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return vpa.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vpa_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(vpa.SYMBOLS), names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_stats_slots_matches_bruteforce(lib):
+    for w in (1, 2, 5, 125, 1000, 16753, 25008):
+        for s in (1, 2, 3, 8):
+            for b in (1, 7, 256, 1024, 8192):
+                if w * s > 200000 and b < 64:
+                    continue
+                want = bf.bf_stats_slots(w, s, b) if w * s <= 20000 else None
+                got = lib.vpa_stats_slots(w, s, b)
+                if want is not None:
+                    assert got == want, (w, s, b)
+                assert got >= 1
+    assert lib.vpa_stats_slots(0, 1, 1) == -1
+    assert lib.vpa_stats_slots(1, 0, 1) == -1
+    assert lib.vpa_stats_slots(1, 1, 0) == -1
+    # the configurations' slot counts
+    assert lib.vpa_stats_slots(76032, 2, 8192) == 10
+    assert lib.vpa_stats_slots(50016, 4, 8192) == 7
+    assert lib.vpa_stats_slots(50016, 4, 1024) == 50
+    assert lib.vpa_stats_slots(25008, 8, 8192) == 4
+    assert lib.vpa_stats_slots(25008, 8, 1024) == 26
+
+
+def V(v, w, s):
+    return vpa.Vocab(v, w, s)
+
+
+def call_block_stats(lib, logits=FAKE, dt=vpa.VPA_BF16, ld=1000, voc=None, first=0, nloc=1,
+                     rows=None, n_rows=4, logits_rows=4, block=256, stats=FAKE):
+    voc = voc or V(1000, 1000, 1)
+    return lib.vpa_block_stats(logits, dt, ld, voc, first, nloc, rows, n_rows, logits_rows, block,
+                               stats, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(voc=V(0, 1, 1)), vpa.VPA_ERR_INVALID),
+    (dict(voc=V(1 << 24, 1 << 24, 1)), vpa.VPA_ERR_INVALID),
+    (dict(voc=V(1000, 0, 1)), vpa.VPA_ERR_INVALID),
+    (dict(voc=V(1000, 100, 0)), vpa.VPA_ERR_INVALID),
+    (dict(voc=V(1000, 100, 9), nloc=1), vpa.VPA_ERR_INVALID),          # 900 < 1000 columns
+    (dict(first=-1), vpa.VPA_ERR_INVALID),
+    (dict(nloc=0), vpa.VPA_ERR_INVALID),
+    (dict(voc=V(1000, 500, 2), first=1, nloc=2), vpa.VPA_ERR_INVALID),
+    (dict(ld=999), vpa.VPA_ERR_INVALID),
+    (dict(block=0), vpa.VPA_ERR_INVALID),
+    (dict(dt=7), vpa.VPA_ERR_UNSUPPORTED),
+    (dict(logits=None), vpa.VPA_ERR_INVALID),
+    (dict(logits=FAKE_ODD), vpa.VPA_ERR_INVALID),
+    (dict(stats=None), vpa.VPA_ERR_INVALID),
+    (dict(stats=FAKE_ODD), vpa.VPA_ERR_INVALID),
+    (dict(n_rows=-1), vpa.VPA_ERR_INVALID),
+    (dict(n_rows=5, logits_rows=4), vpa.VPA_ERR_INVALID),               # identity rows past the buffer
+    (dict(voc=V(100, 100, 1), ld=100, block=1, n_rows=1 << 25, logits_rows=1 << 25), vpa.VPA_ERR_INVALID),
+])
+def test_block_stats_rejects(lib, kw, status):
+    assert call_block_stats(lib, **kw) == status
+    assert vpa.last_error() != ""
+
+
+def test_block_stats_ld_covers_only_valid_columns(lib):
+    # the last rank of V=1000 over W=334, S=3 holds 332 valid columns; ld=332 is enough,
+    # and a zero-row call is a no-op that never touches the pointers
+    assert call_block_stats(lib, voc=V(1000, 334, 3), first=2, nloc=1, ld=332, n_rows=0) == vpa.VPA_OK
+    assert call_block_stats(lib, voc=V(1000, 334, 3), first=2, nloc=1, ld=331, n_rows=0) == vpa.VPA_ERR_INVALID
+
+
+def test_empty_batches_are_noops(lib):
+    assert call_block_stats(lib, n_rows=0, stats=None) == vpa.VPA_OK
+    assert lib.vpa_combine_stats(None, 8, 0, 2, None, None, None) == vpa.VPA_OK
+    assert lib.vpa_top_tokens(FAKE, vpa.VPA_BF16, 1000, V(1000, 125, 8), 0, 256, None, 0, None,
+                              None, None) == vpa.VPA_OK
+    assert lib.vpa_verify_stats(FAKE, vpa.VPA_F32, 1000, V(1000, 125, 8), 0, 8, 0, 3, 8192, 1024,
+                                None, None, None) == vpa.VPA_OK
+    assert lib.vpa_greedy_verify(None, 1, None, 1, 8, 0, 3, None, None, None, None, None,
+                                 None) == vpa.VPA_OK
+
+
+def test_combine_rejects(lib):
+    assert lib.vpa_combine_stats(FAKE, 0, 4, 2, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert lib.vpa_combine_stats(FAKE, 2, 4, 0, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert lib.vpa_combine_stats(None, 2, 4, 2, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert lib.vpa_combine_stats(FAKE, 2, 4, 2, None, None, None) == vpa.VPA_ERR_INVALID
+    assert lib.vpa_combine_stats(FAKE, 2, 4, 2, FAKE, FAKE_ODD, None) == vpa.VPA_ERR_INVALID
+    assert lib.vpa_combine_stats(FAKE, 2, -1, 2, FAKE, None, None) == vpa.VPA_ERR_INVALID
+
+
+def test_top_tokens_rejects(lib):
+    voc = V(151936, 76032, 2)
+    need = lib.vpa_top_tokens_workspace(voc, 32, 8192)
+    assert need == 2 * 32 * 10 * 8
+    assert lib.vpa_top_tokens_workspace(voc, 0, 8192) == 0
+    assert lib.vpa_top_tokens_workspace(voc, 32, 0) == 0
+    args = dict(ld=152064, n=32, block=8192, ws=FAKE, wsb=need, ids=FAKE)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return lib.vpa_top_tokens(FAKE, vpa.VPA_BF16, a["ld"], voc, a["n"], a["block"], a["ws"],
+                                  a["wsb"], a["ids"], None, None)
+    assert call(wsb=need - 1) == vpa.VPA_ERR_INVALID
+    assert call(ws=None) == vpa.VPA_ERR_INVALID
+    assert call(ws=FAKE_ODD) == vpa.VPA_ERR_INVALID
+    assert call(ids=None) == vpa.VPA_ERR_INVALID
+    assert call(ld=151935) == vpa.VPA_ERR_INVALID
+    assert call(block=-3) == vpa.VPA_ERR_INVALID
+    assert "workspace" in (call(wsb=1) and vpa.last_error())
+
+
+def test_verify_rejects(lib):
+    voc = V(200064, 50016, 4)
+    assert lib.vpa_verify_stats(FAKE, vpa.VPA_BF16, 200064, voc, 0, 4, 24, 0, 8192, 1024, FAKE,
+                                FAKE, None) == vpa.VPA_ERR_INVALID
+    assert lib.vpa_verify_stats(FAKE, vpa.VPA_BF16, 200064, voc, 0, 4, 24, 3, 0, 1024, FAKE,
+                                FAKE, None) == vpa.VPA_ERR_INVALID
+    assert lib.vpa_verify_stats(FAKE, vpa.VPA_BF16, 200064, voc, 0, 4, 24, 3, 8192, 1024, None,
+                                FAKE, None) == vpa.VPA_ERR_INVALID
+    gv = lib.vpa_greedy_verify
+    assert gv(FAKE, 7, FAKE, 50, 4, 24, 0, FAKE, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert gv(FAKE, 0, FAKE, 50, 4, 24, 3, FAKE, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert gv(FAKE, 7, FAKE, 50, 0, 24, 3, FAKE, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert gv(FAKE, 7, FAKE, 50, 4, 24, 3, None, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert gv(FAKE, 7, FAKE, 50, 4, 24, 3, FAKE, FAKE, FAKE, FAKE, FAKE_ODD, None) == vpa.VPA_ERR_INVALID
+    assert gv(FAKE, 7, FAKE, 50, 4, -1, 3, FAKE, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
+
+
+def test_last_error_is_per_call_message(lib):
+    call_block_stats(lib, block=0)
+    assert "block" in vpa.last_error()

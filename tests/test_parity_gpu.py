@@ -1,0 +1,235 @@
+"""GPU parity: every output of the HIP path (statistics, token ids, value bits,
+verification outputs) must equal the CPU oracle's bit for bit, on the same
+seeded inputs.  The inputs are generated on the CPU (workloads.py), copied to
+the device for the HIP path, and handed unchanged to the oracle."""
+import random
+
+import pytest
+import torch
+
+import oracle
+import oracle_pins
+import vocab_argmax_amd as vpa
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _announce(msg):
+    print(f"[parity] {msg}", flush=True)
+
+
+def _dev(x):
+    return x.to(DEV)
+
+
+def _host(x):
+    torch.cuda.synchronize()
+    return x.cpu()
+
+
+def assert_same(got, want, what):
+    got = _host(got)
+    if not torch.equal(got, want):
+        bad = (got != want).nonzero()
+        raise AssertionError(f"{what}: {bad.shape[0]} mismatches, first at {bad[:4].tolist()}")
+
+
+def check_stats_and_ids(x_cpu, vocab, w, s, block, name):
+    """block_stats (all shards, then rank by rank), combine and top_tokens."""
+    _announce(f"{name} block={block}")
+    x = _dev(x_cpu)
+    want_stats = oracle.block_stats(x_cpu, vocab, w, s, block)
+    want_ids, want_vals = oracle.argmax(x_cpu, vocab)
+    st = vpa.block_stats(x, vocab, w, s, block)
+    assert_same(st, want_stats, f"{name} stats B={block}")
+    ids, vals = vpa.combine_stats(st)
+    assert_same(ids, want_ids, f"{name} combine ids")
+    assert_same(vals.to(torch.int64) & 0xFFFFFFFF, want_vals, f"{name} combine vals")
+    ids, vals = vpa.top_tokens(x, vocab, w, s, block)
+    assert_same(ids, want_ids, f"{name} top_tokens ids")
+    assert_same(vals.to(torch.int64) & 0xFFFFFFFF, want_vals, f"{name} top_tokens vals")
+    # each rank reduces only its own columns (global ids, global block edges)
+    parts = []
+    for r in range(s):
+        xr = x[:, r * w:min((r + 1) * w, x.shape[1])]
+        parts.append(vpa.block_stats(xr, vocab, w, s, block, first_shard=r, n_local=1))
+    assert_same(torch.cat(parts, 0), want_stats, f"{name} rank-wise stats")
+
+
+def test_config1_argmax_v1000_fp32():
+    w = workloads.config1()
+    check_stats_and_ids(w.logits, w.vocab, w.shard_width, w.n_shards, 256, w.name)
+    ids, _ = vpa.top_tokens(_dev(w.logits), w.vocab, w.shard_width, w.n_shards, 256)
+    assert _host(ids)[[1, 3]].tolist() == [17, 17]
+
+
+@pytest.mark.parametrize("case", workloads.edge_cases(), ids=lambda c: c.name)
+def test_edge_cases(case):
+    for b in case.blocks:
+        check_stats_and_ids(case.logits, case.vocab, case.shard_width, case.n_shards, b, case.name)
+
+
+def _verify_both(x_cpu, vocab, w, s, n_req, k, drafts, bd, bb, name):
+    _announce(f"{name} verify R={n_req} K={k} blocks={bd}/{bb}")
+    x = _dev(x_cpu)
+    draft_rows, bonus_rows = oracle.verify_rows(n_req, k)
+    want_d = oracle.block_stats(x_cpu, vocab, w, s, bd, rows=draft_rows)
+    want_b = oracle.block_stats(x_cpu, vocab, w, s, bb, rows=bonus_rows)
+    dst, bst = vpa.verify_stats(x, vocab, w, s, n_req, k, bd, bb)
+    assert_same(dst, want_d, f"{name} draft stats")
+    assert_same(bst, want_b, f"{name} bonus stats")
+    want = oracle.greedy_verify(want_d, want_b, drafts)
+    want_logits = oracle.greedy_verify_logits(x_cpu, vocab, drafts)
+    for a, b in zip(want, want_logits):
+        assert torch.equal(a, b)
+    got = vpa.greedy_verify(dst, bst, _dev(drafts))
+    for g, wv, nm in zip(got, want, ("out_tokens", "num_sampled", "num_rejected", "target_ids")):
+        assert_same(g, wv, f"{name} {nm}")
+    got_nt = vpa.greedy_verify(dst, bst, _dev(drafts), with_targets=False)
+    for g, wv in zip(got_nt[:3], want[:3]):
+        assert_same(g, wv, f"{name} (no target_ids)")
+    # block_stats with explicit row lists gives the same statistics
+    assert_same(vpa.block_stats(x, vocab, w, s, bd, rows=_dev(draft_rows)), want_d, f"{name} rows")
+    return want
+
+
+@pytest.mark.parametrize("case", workloads.edge_cases(), ids=lambda c: c.name)
+def test_edge_verify(case):
+    x, v, w, s = case.logits, case.vocab, case.shard_width, case.n_shards
+    tgt, _ = oracle.argmax(x, v)
+    for k in (1, 5):
+        for plan, uniform in workloads.edge_verify_plans(k, v):
+            n_req = plan.shape[0]
+            targets = tgt[:n_req * (k + 1)].reshape(n_req, k + 1)
+            drafts = workloads.compose_drafts(targets, plan, uniform)
+            for bd, bb in ((8192, 1024), (256, 1000)):
+                _verify_both(x, v, w, s, n_req, k, drafts, bd, bb, case.name)
+
+
+def test_row_list_out_of_range_rows_are_empty():
+    case = workloads.edge_cases()[3]                      # vocab 1000, 8 shards, bf16
+    x = _dev(case.logits)
+    rows = torch.tensor([3, 0, -1, 16, 15, 1 << 30], dtype=torch.int32)
+    st = _host(vpa.block_stats(x, case.vocab, case.shard_width, case.n_shards, 256, rows=_dev(rows)))
+    want = oracle.block_stats(case.logits, case.vocab, case.shard_width, case.n_shards, 256,
+                              rows=torch.tensor([3, 0, 15]))
+    assert torch.equal(st[:, [0, 1, 4]], want)
+    for i in (2, 3, 5):
+        assert bool((st[:, i, :, 0] == torch.tensor(vpa.EMPTY_BITS).to(torch.int32)).all())
+        assert bool((st[:, i, :, 1] == vpa.EMPTY_ID).all())
+
+
+def _random_case(rng, trial):
+    """A padded [rows, S*W + pad] matrix and a column offset `off` <= pad: the
+    case is the view full[:, off:], whose base is misaligned by `off` elements
+    and whose valid columns stay inside the buffer."""
+    dtype = torch.float32 if trial % 2 else torch.bfloat16
+    s = rng.choice([1, 2, 3, 4, 5, 8])
+    vocab = rng.choice([1, 2, 7, 63, 1000, 4097, 50257, 70001])
+    w = -(-vocab // s) + rng.choice([0, 0, 1, 3, 64])
+    block = rng.choice([1, 3, 64, 255, 256, 1000, 1024, 8192, 65536, 1 << 20])
+    if vocab > 10000 and block < 64:
+        block = 64
+    pad = rng.choice([0, 1, 5, 8])
+    off = rng.randint(0, pad)
+    n_rows = rng.choice([1, 3, 9])
+    full = oracle_pins._special_matrix(n_rows, s * w + pad, 9000 + trial, dtype)
+    full[:, vocab:s * w] = float("nan")
+    return full, off, vocab, w, s, block
+
+
+def test_random_geometries():
+    """Random V, S, W, block, dtype, row padding and base misalignment."""
+    rng = random.Random(1234)
+    for trial in range(80):
+        full, off, vocab, w, s, block = _random_case(rng, trial)
+        x_cpu = full[:, off:]
+        x = _dev(full)[:, off:]
+        name = f"random{trial} V={vocab} S={s} W={w} B={block} ld={full.shape[1]} off={off} {full.dtype}"
+        _announce(name)
+        want_stats = oracle.block_stats(x_cpu, vocab, w, s, block)
+        assert_same(vpa.block_stats(x, vocab, w, s, block), want_stats, name)
+        want_ids, want_vals = oracle.argmax(x_cpu, vocab)
+        ids, vals = vpa.top_tokens(x, vocab, w, s, block)
+        assert_same(ids, want_ids, name + " ids")
+        assert_same(vals.to(torch.int64) & 0xFFFFFFFF, want_vals, name + " vals")
+
+
+def test_long_segments_and_chunk_cascade():
+    """Blocks far larger than 16 wave iterations (the chunk loop) and every
+    remainder size of the 8/4/2/1 cascade, with ties planted far apart."""
+    for dtype in (torch.bfloat16, torch.float32):
+        for vocab, s, block in ((200064, 2, 1 << 20), (200064, 1, 1 << 21), (131071, 3, 65536),
+                                (9000, 1, 9000), (5000, 1, 4608)):
+            w = -(-vocab // s)
+            g = torch.Generator().manual_seed(vocab + s)
+            x = (torch.randn((4, s * w), generator=g) * 3).to(dtype)
+            x[:, vocab:] = float("nan")
+            x[1, 5] = 100.0
+            x[1, vocab - 3] = 100.0
+            x[2, vocab // 2] = float("nan")
+            x[2, vocab - 1] = float("nan")
+            x[3, :vocab] = float("-inf")
+            check_stats_and_ids(x, vocab, w, s, block, f"long V={vocab} S={s} B={block} {dtype}")
+
+
+def test_config2_top_tokens_v151936_bf16_tp2():
+    w = workloads.config2()
+    check_stats_and_ids(w.logits, w.vocab, w.shard_width, w.n_shards, 8192, w.name)
+
+
+def test_config3_verify_v200064_bf16_tp4():
+    w = workloads.config3()
+    tgt, _ = oracle.argmax(w.logits, w.vocab)
+    drafts = workloads.compose_drafts(tgt.reshape(w.n_req, w.k + 1), w.draft_plan, w.draft_uniform)
+    want = _verify_both(w.logits, w.vocab, w.shard_width, w.n_shards, w.n_req, w.k, drafts, 8192,
+                        1024, w.name)
+    # the plan copies the target with p=0.7: some but not all drafts accepted
+    assert 0 < int(want[2].sum()) < w.n_req * w.k
+
+
+def test_config4_full_size_4096_rows():
+    """4096 x 200064 bf16 at 8 shards, in the launch shapes the benchmark times."""
+    w = workloads.config4()
+    _announce(f"{w.name}: oracle argmax")
+    want_ids, want_vals = oracle.argmax(w.logits, w.vocab)
+    x = _dev(w.logits)
+    ids, vals = vpa.top_tokens(x, w.vocab, w.shard_width, w.n_shards, 8192)
+    assert_same(ids, want_ids, "config4 ids")
+    assert_same(vals.to(torch.int64) & 0xFFFFFFFF, want_vals, "config4 vals")
+    _announce(f"{w.name}: oracle block stats")
+    want_stats = oracle.block_stats(w.logits, w.vocab, w.shard_width, w.n_shards, 8192)
+    assert_same(vpa.block_stats(x, w.vocab, w.shard_width, w.n_shards, 8192), want_stats, "config4 stats")
+    drafts = workloads.compose_drafts(want_ids[:w.n_req * (w.k + 1)].reshape(w.n_req, w.k + 1),
+                                      w.draft_plan, w.draft_uniform)
+    _verify_both(w.logits, w.vocab, w.shard_width, w.n_shards, w.n_req, w.k, drafts, 8192, 1024,
+                 w.name)
+
+
+def test_repeat_runs_are_bitwise_identical():
+    w = workloads.config2()
+    x = _dev(w.logits)
+    first = [t.clone() for t in vpa.top_tokens(x, w.vocab, w.shard_width, w.n_shards, 8192)]
+    st0 = vpa.block_stats(x, w.vocab, w.shard_width, w.n_shards, 1024).clone()
+    for _ in range(5):
+        again = vpa.top_tokens(x, w.vocab, w.shard_width, w.n_shards, 8192)
+        for a, b in zip(first, again):
+            assert torch.equal(a, b)
+        assert torch.equal(st0, vpa.block_stats(x, w.vocab, w.shard_width, w.n_shards, 1024))
+
+
+def test_empty_batch_gpu():
+    x = torch.empty((0, 1000), dtype=torch.bfloat16, device=DEV)
+    st = vpa.block_stats(x, 1000, 125, 8, 256)
+    assert st.shape == (8, 0, 2, 2)
+    ids, vals = vpa.top_tokens(x, 1000, 125, 8, 256)
+    assert ids.numel() == 0
+    ids, vals = vpa.combine_stats(st)
+    assert ids.numel() == 0
+    dst, bst = vpa.verify_stats(x, 1000, 125, 8, 0, 3)
+    out, ns, nr, tg = vpa.greedy_verify(dst, bst, torch.empty((0, 3), dtype=torch.int32, device=DEV))
+    assert out.shape == (0, 4)
+    torch.cuda.synchronize()

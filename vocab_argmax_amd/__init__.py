@@ -1,0 +1,275 @@
+"""vocab_argmax_amd -- vocab-parallel greedy argmax and greedy verification on
+MI355X (gfx950).
+
+A thin ctypes binding over libvpa.so, whose C ABI is include/vpa.h.  This
+module only marshals arguments: it checks devices, dtypes and strides, passes
+``data_ptr()`` and the current HIP stream, and allocates outputs with torch.
+Every step of the computation runs in the library's HIP kernels; there is no
+fallback.  If libvpa.so is missing, every call raises.
+
+Statistics tensors are int32 of shape [shards][rows][M][2]: word 0 holds the
+fp32 bit pattern of the block maximum, word 1 its global token id (the
+library's ``vpa_stat``).  Value bits come back as int32 tensors holding fp32
+bit patterns; ``.view(torch.float32)`` reads them as values.
+
+Sources: vLLM PR #34049, "Solution" (per-shard argmax, exchange of
+(max value, global index) pairs, reduction over ranks) and vLLM PR #62604,
+"Purpose" items 1 and 2 (per-block statistics with global block boundaries,
+fused get_top_tokens, greedy verification) and "Test Plan" (rank-order
+layout of the statistics).
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvpa.so")
+
+VPA_OK, VPA_ERR_INVALID, VPA_ERR_UNSUPPORTED, VPA_ERR_HIP = 0, 1, 2, 3
+VPA_F32, VPA_BF16 = 0, 1
+EMPTY_BITS = 0xFF800000
+EMPTY_ID = 0x7FFFFFFF
+DRAFT_BLOCK = 8192   # global block size for draft positions (PR #62604, "Purpose" item 1)
+BONUS_BLOCK = 1024   # global block size for the bonus position
+
+# Every symbol include/vpa.h declares.
+SYMBOLS = ("vpa_stats_slots", "vpa_block_stats", "vpa_verify_stats", "vpa_combine_stats",
+           "vpa_top_tokens_workspace", "vpa_top_tokens", "vpa_greedy_verify", "vpa_last_error")
+
+
+class VpaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"vpa status {status}: {message}")
+        self.status = status
+
+
+class Vocab(ctypes.Structure):
+    """vpa_vocab: V valid columns, S shards of W columns."""
+    _fields_ = [("vocab", ctypes.c_int64), ("shard_width", ctypes.c_int64),
+                ("n_shards", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def _bind(lib):
+    i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+    st = ctypes.c_int
+    lib.vpa_stats_slots.argtypes = [i64, i32, i32]
+    lib.vpa_stats_slots.restype = i32
+    lib.vpa_block_stats.argtypes = [vp, ctypes.c_int, i64, Vocab, i32, i32, vp, i64, i64, i32, vp, vp]
+    lib.vpa_block_stats.restype = st
+    lib.vpa_verify_stats.argtypes = [vp, ctypes.c_int, i64, Vocab, i32, i32, i64, i32, i32, i32,
+                                     vp, vp, vp]
+    lib.vpa_verify_stats.restype = st
+    lib.vpa_combine_stats.argtypes = [vp, i32, i64, i32, vp, vp, vp]
+    lib.vpa_combine_stats.restype = st
+    lib.vpa_top_tokens_workspace.argtypes = [Vocab, i64, i32]
+    lib.vpa_top_tokens_workspace.restype = sz
+    lib.vpa_top_tokens.argtypes = [vp, ctypes.c_int, i64, Vocab, i64, i32, vp, sz, vp, vp, vp]
+    lib.vpa_top_tokens.restype = st
+    lib.vpa_greedy_verify.argtypes = [vp, i32, vp, i32, i32, i64, i32, vp, vp, vp, vp, vp, vp]
+    lib.vpa_greedy_verify.restype = st
+    lib.vpa_last_error.argtypes = []
+    lib.vpa_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+def lib():
+    """The loaded libvpa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m vocab_argmax_amd._build` (hipcc, gfx950)")
+        _lib = _bind(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def last_error() -> str:
+    return lib().vpa_last_error().decode()
+
+
+def _check(status):
+    if status != VPA_OK:
+        raise VpaError(status, last_error())
+
+
+def _vp(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(x):
+    if x.dtype == torch.bfloat16:
+        return VPA_BF16
+    if x.dtype == torch.float32:
+        return VPA_F32
+    raise TypeError(f"logits must be bfloat16 or float32, not {x.dtype}")
+
+
+def _logits_ld(x):
+    if not x.is_cuda:
+        raise ValueError("logits must be a device tensor")
+    if x.dim() != 2:
+        raise ValueError("logits must be 2-D [rows, columns]")
+    if x.shape[1] > 1 and x.stride(1) != 1:
+        raise ValueError("logits columns must be contiguous (stride 1)")
+    return x.stride(0) if x.shape[0] > 1 else x.shape[1]
+
+
+def _int32_dev(t, name, device):
+    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, logits on {device}")
+    return t
+
+
+def _stats_tensor(t, name):
+    if t.dtype != torch.int32 or t.dim() != 4 or t.shape[3] != 2 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 [shards][rows][M][2] tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return t
+
+
+def stats_slots(shard_width: int, n_shards: int, block: int) -> int:
+    """M: statistic slots per shard (the most global blocks a shard touches)."""
+    m = lib().vpa_stats_slots(shard_width, n_shards, block)
+    if m < 0:
+        raise ValueError("invalid shard_width / n_shards / block")
+    return m
+
+
+def block_stats(logits, vocab, shard_width, n_shards, block, rows=None, first_shard=0,
+                n_local=None, out=None, stream=None):
+    """Per-block statistics of shards first_shard..first_shard+n_local-1.
+
+    logits [R, ld]: column 0 is global column first_shard*W.  rows: optional
+    int32 device tensor of row indices.  Returns int32 [n_local][n_rows][M][2].
+    """
+    ld = _logits_ld(logits)
+    if n_local is None:
+        n_local = n_shards - first_shard
+    if rows is not None:
+        rows = _int32_dev(rows, "rows", logits.device)
+    n_rows = logits.shape[0] if rows is None else rows.numel()
+    m = stats_slots(shard_width, n_shards, block)
+    if out is None:
+        out = torch.empty((n_local, n_rows, m, 2), dtype=torch.int32, device=logits.device)
+    _stats_tensor(out, "out")
+    if tuple(out.shape) != (n_local, n_rows, m, 2):
+        raise ValueError(f"out has shape {tuple(out.shape)}, expected {(n_local, n_rows, m, 2)}")
+    _check(lib().vpa_block_stats(_vp(logits), _dtype_code(logits), ld,
+                                 Vocab(vocab, shard_width, n_shards), first_shard, n_local,
+                                 _vp(rows), n_rows, logits.shape[0], block, _vp(out),
+                                 _stream(stream)))
+    return out
+
+
+def verify_stats(logits, vocab, shard_width, n_shards, n_req, k, block_draft=DRAFT_BLOCK,
+                 block_bonus=BONUS_BLOCK, first_shard=0, n_local=None, out=None, stream=None):
+    """Draft- and bonus-row statistics of a verification batch in one launch.
+
+    Request r owns rows r*(K+1)..r*(K+1)+K of logits.  Returns
+    (draft_stats [n_local][n_req*K][Md][2], bonus_stats [n_local][n_req][Mb][2]);
+    `out` may supply that pair preallocated.
+    """
+    ld = _logits_ld(logits)
+    if n_local is None:
+        n_local = n_shards - first_shard
+    if logits.shape[0] < n_req * (k + 1):
+        raise ValueError(f"logits has {logits.shape[0]} rows, need {n_req * (k + 1)}")
+    md = stats_slots(shard_width, n_shards, block_draft)
+    mb = stats_slots(shard_width, n_shards, block_bonus)
+    if out is None:
+        dst = torch.empty((n_local, n_req * k, md, 2), dtype=torch.int32, device=logits.device)
+        bst = torch.empty((n_local, n_req, mb, 2), dtype=torch.int32, device=logits.device)
+    else:
+        dst, bst = out
+        if (tuple(dst.shape) != (n_local, n_req * k, md, 2)
+                or tuple(bst.shape) != (n_local, n_req, mb, 2)):
+            raise ValueError("preallocated verification statistics have the wrong shape")
+    _stats_tensor(dst, "draft_stats")
+    _stats_tensor(bst, "bonus_stats")
+    _check(lib().vpa_verify_stats(_vp(logits), _dtype_code(logits), ld,
+                                  Vocab(vocab, shard_width, n_shards), first_shard, n_local, n_req,
+                                  k, block_draft, block_bonus, _vp(dst), _vp(bst), _stream(stream)))
+    return dst, bst
+
+
+def combine_stats(stats, stream=None):
+    """Rank-order combination of [S][N][M][2] statistics -> (ids int32[N], val_bits int32[N])."""
+    _stats_tensor(stats, "stats")
+    s, n, m, _ = stats.shape
+    ids = torch.empty(n, dtype=torch.int32, device=stats.device)
+    vals = torch.empty(n, dtype=torch.int32, device=stats.device)
+    _check(lib().vpa_combine_stats(_vp(stats), s, n, m, _vp(ids), _vp(vals), _stream(stream)))
+    return ids, vals
+
+
+def top_tokens_workspace(vocab, shard_width, n_shards, n_rows, block=DRAFT_BLOCK) -> int:
+    return int(lib().vpa_top_tokens_workspace(Vocab(vocab, shard_width, n_shards), n_rows, block))
+
+
+def top_tokens(logits, vocab, shard_width, n_shards, block=DRAFT_BLOCK, workspace=None,
+               ids=None, val_bits=None, stream=None):
+    """Fused get_top_tokens over all shards of each row -> (ids int32[N], val_bits int32[N]).
+
+    logits [N, ld] holds the S shards side by side (ld >= vocab).  workspace:
+    optional uint8 device tensor of at least top_tokens_workspace() bytes.
+    """
+    ld = _logits_ld(logits)
+    n = logits.shape[0]
+    need = top_tokens_workspace(vocab, shard_width, n_shards, n, block)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=logits.device)
+    if ids is None:
+        ids = torch.empty(n, dtype=torch.int32, device=logits.device)
+    if val_bits is None:
+        val_bits = torch.empty(n, dtype=torch.int32, device=logits.device)
+    _check(lib().vpa_top_tokens(_vp(logits), _dtype_code(logits), ld,
+                                Vocab(vocab, shard_width, n_shards), n, block, _vp(workspace),
+                                workspace.numel() * workspace.element_size(), _vp(ids),
+                                _vp(val_bits), _stream(stream)))
+    return ids, val_bits
+
+
+def greedy_verify(draft_stats, bonus_stats, draft_ids, with_targets=True, out=None,
+                  stream=None):
+    """Greedy verification from gathered statistics.
+
+    draft_stats [S][R*K][Md][2], bonus_stats [S][R][Mb][2], draft_ids int32 [R][K].
+    Returns (out_tokens [R][K+1], num_sampled [R], num_rejected [R], target_ids [R][K+1] or None);
+    `out` may supply those four tensors preallocated (the last may be None).
+    """
+    _stats_tensor(draft_stats, "draft_stats")
+    _stats_tensor(bonus_stats, "bonus_stats")
+    dev = draft_stats.device
+    _int32_dev(draft_ids, "draft_ids", dev)
+    r, k = draft_ids.shape
+    s = draft_stats.shape[0]
+    if bonus_stats.shape[0] != s or draft_stats.shape[1] != r * k or bonus_stats.shape[1] != r:
+        raise ValueError("statistics shapes do not match draft_ids [R][K]")
+    if out is None:
+        out_t = torch.empty((r, k + 1), dtype=torch.int32, device=dev)
+        ns = torch.empty(r, dtype=torch.int32, device=dev)
+        nr = torch.empty(r, dtype=torch.int32, device=dev)
+        tg = torch.empty((r, k + 1), dtype=torch.int32, device=dev) if with_targets else None
+    else:
+        out_t, ns, nr, tg = out
+        for t, shape in ((out_t, (r, k + 1)), (ns, (r,)), (nr, (r,)), (tg, (r, k + 1))):
+            if t is not None and (tuple(t.shape) != shape or t.dtype != torch.int32
+                                  or not t.is_contiguous()):
+                raise ValueError("preallocated verification outputs have the wrong shape/dtype")
+    _check(lib().vpa_greedy_verify(_vp(draft_stats), draft_stats.shape[2], _vp(bonus_stats),
+                                   bonus_stats.shape[2], s, r, k, _vp(draft_ids), _vp(out_t),
+                                   _vp(ns), _vp(nr), _vp(tg), _stream(stream)))
+    return out_t, ns, nr, tg

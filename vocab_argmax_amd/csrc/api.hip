@@ -1,0 +1,300 @@
+// api.hip -- the C ABI of include/vpa.h: host-side validation, sizing and
+// launches.  No HIP call happens before every argument has been checked, so
+// invalid calls enqueue nothing and can be exercised without a GPU.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "vpa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+vpa_status fail(vpa_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+vpa_status hip_fail(hipError_t e, const char* what) {
+    return fail(VPA_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+vpa_status ok() {
+    return VPA_OK;
+}
+
+int esize_of(vpa_dtype dt) {
+    return dt == VPA_BF16 ? 2 : (dt == VPA_F32 ? 4 : 0);
+}
+
+bool aligned(const void* p, size_t a) {
+    return ((uintptr_t)p % a) == 0;
+}
+
+// Slots per shard M (the most global blocks any shard touches), -1 if invalid.
+int64_t slots(int64_t w, int64_t s, int64_t b) {
+    if (w < 1 || s < 1 || b < 1)
+        return -1;
+    int64_t m = 0;
+    for (int64_t i = 0; i < s; ++i) {
+        const int64_t lo = i * w;
+        const int64_t n = (lo + w - 1) / b - lo / b + 1;
+        if (n > m)
+            m = n;
+    }
+    return m;
+}
+
+vpa_status check_vocab(const vpa_vocab& v) {
+    if (v.vocab < 1 || v.vocab >= VPA_MAX_VOCAB)
+        return fail(VPA_ERR_INVALID, "vocab %lld outside [1, 2^24)", (long long)v.vocab);
+    if (v.shard_width < 1 || v.shard_width > INT32_MAX)
+        return fail(VPA_ERR_INVALID, "shard_width %lld outside [1, 2^31)", (long long)v.shard_width);
+    if (v.n_shards < 1)
+        return fail(VPA_ERR_INVALID, "n_shards %d < 1", (int)v.n_shards);
+    if ((int64_t)v.n_shards * v.shard_width < v.vocab)
+        return fail(VPA_ERR_INVALID, "n_shards*shard_width = %lld does not cover vocab %lld",
+                    (long long)((int64_t)v.n_shards * v.shard_width), (long long)v.vocab);
+    return ok();
+}
+
+vpa_status check_dtype(vpa_dtype dt) {
+    if (esize_of(dt) == 0)
+        return fail(VPA_ERR_UNSUPPORTED, "dtype %d is not VPA_F32 or VPA_BF16", (int)dt);
+    return ok();
+}
+
+// Shared checks of the logits-reading calls; fills `t` with the geometry.
+vpa_status check_logits_task(const void* logits, vpa_dtype dt, int64_t ld, const vpa_vocab& v,
+                             int32_t first_shard, int32_t n_local, int32_t block,
+                             vpa::SegTask& t) {
+    vpa_status st;
+    if ((st = check_dtype(dt)) != VPA_OK)
+        return st;
+    if ((st = check_vocab(v)) != VPA_OK)
+        return st;
+    if (first_shard < 0 || n_local < 1 || (int64_t)first_shard + n_local > v.n_shards)
+        return fail(VPA_ERR_INVALID, "shard range [%d, %d+%d) outside [0, %d)", (int)first_shard,
+                    (int)first_shard, (int)n_local, (int)v.n_shards);
+    if (block < 1)
+        return fail(VPA_ERR_INVALID, "block %d < 1", (int)block);
+    const int64_t col0 = (int64_t)first_shard * v.shard_width;
+    int64_t need = (int64_t)n_local * v.shard_width;
+    if (v.vocab - col0 < need)
+        need = v.vocab - col0;
+    if (need < 1)
+        need = 1;
+    if (ld < need)
+        return fail(VPA_ERR_INVALID, "ld %lld < %lld valid local columns", (long long)ld,
+                    (long long)need);
+    t = vpa::SegTask{};
+    t.base = (const unsigned char*)logits;
+    t.ld = ld;
+    t.vocab = v.vocab;
+    t.shard_width = v.shard_width;
+    t.col0 = col0;
+    t.first_shard = first_shard;
+    t.n_local = n_local;
+    t.block = block;
+    t.m = (int32_t)slots(v.shard_width, v.n_shards, block);
+    return ok();
+}
+
+// Pointer checks of the logits, made only when there is work (an empty batch
+// may pass the NULL data pointer of an empty tensor).
+vpa_status check_logits_ptr(const void* logits, vpa_dtype dt) {
+    if (!logits)
+        return fail(VPA_ERR_INVALID, "logits is NULL");
+    if (!aligned(logits, (size_t)esize_of(dt)))
+        return fail(VPA_ERR_INVALID, "logits not aligned to its element size");
+    return ok();
+}
+
+vpa_status set_items(vpa::SegTask& t, int64_t n_rows, const char* what) {
+    const int64_t items = n_rows * t.n_local * (int64_t)t.m;
+    if (n_rows > INT32_MAX || items > INT32_MAX)
+        return fail(VPA_ERR_INVALID, "%s: %lld statistics exceed 2^31-1 per call", what,
+                    (long long)items);
+    t.n_rows = (int32_t)n_rows;
+    t.n_items = (int32_t)items;
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t vpa_stats_slots(int64_t shard_width, int32_t n_shards, int32_t block) {
+    const int64_t m = slots(shard_width, n_shards, block);
+    return m > INT32_MAX ? -1 : (int32_t)m;
+}
+
+vpa_status vpa_block_stats(const void* logits, vpa_dtype dtype, int64_t ld, vpa_vocab v,
+                           int32_t first_shard, int32_t n_local_shards, const int32_t* rows,
+                           int64_t n_rows, int64_t logits_rows, int32_t block, vpa_stat* stats,
+                           void* stream) {
+    vpa::SegTask t;
+    vpa_status st = check_logits_task(logits, dtype, ld, v, first_shard, n_local_shards, block, t);
+    if (st != VPA_OK)
+        return st;
+    if (n_rows < 0)
+        return fail(VPA_ERR_INVALID, "n_rows %lld < 0", (long long)n_rows);
+    if (rows ? logits_rows < 0 : logits_rows < n_rows)
+        return fail(VPA_ERR_INVALID, "logits_rows %lld too small", (long long)logits_rows);
+    if ((st = set_items(t, n_rows, "vpa_block_stats")) != VPA_OK)
+        return st;
+    if (n_rows == 0)
+        return ok();
+    if ((st = check_logits_ptr(logits, dtype)) != VPA_OK)
+        return st;
+    if (!stats || !aligned(stats, 8))
+        return fail(VPA_ERR_INVALID, "stats is NULL or not 8-byte aligned");
+    if (rows && !aligned(rows, 4))
+        return fail(VPA_ERR_INVALID, "rows not 4-byte aligned");
+    t.rows = rows;
+    t.logits_rows = logits_rows;
+    t.stats = stats;
+    vpa::SegTask none{};
+    hipError_t e = vpa::launch_block_stats(esize_of(dtype), t, none, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "vpa_block_stats launch");
+}
+
+vpa_status vpa_verify_stats(const void* logits, vpa_dtype dtype, int64_t ld, vpa_vocab v,
+                            int32_t first_shard, int32_t n_local_shards, int64_t n_req, int32_t k,
+                            int32_t block_draft, int32_t block_bonus, vpa_stat* draft_stats,
+                            vpa_stat* bonus_stats, void* stream) {
+    vpa::SegTask td, tb;
+    vpa_status st;
+    if ((st = check_logits_task(logits, dtype, ld, v, first_shard, n_local_shards, block_draft,
+                                td)) != VPA_OK)
+        return st;
+    if ((st = check_logits_task(logits, dtype, ld, v, first_shard, n_local_shards, block_bonus,
+                                tb)) != VPA_OK)
+        return st;
+    if (k < 1)
+        return fail(VPA_ERR_INVALID, "k %d < 1", (int)k);
+    if (n_req < 0 || n_req * (int64_t)(k + 1) > INT32_MAX)
+        return fail(VPA_ERR_INVALID, "n_req %lld out of range", (long long)n_req);
+    if ((st = set_items(td, n_req * k, "vpa_verify_stats (draft rows)")) != VPA_OK)
+        return st;
+    if ((st = set_items(tb, n_req, "vpa_verify_stats (bonus rows)")) != VPA_OK)
+        return st;
+    if ((int64_t)td.n_items + tb.n_items > INT32_MAX)
+        return fail(VPA_ERR_INVALID, "vpa_verify_stats: too many statistics per call");
+    if (n_req == 0)
+        return ok();
+    if ((st = check_logits_ptr(logits, dtype)) != VPA_OK)
+        return st;
+    if (!draft_stats || !bonus_stats || !aligned(draft_stats, 8) || !aligned(bonus_stats, 8))
+        return fail(VPA_ERR_INVALID, "draft_stats/bonus_stats NULL or not 8-byte aligned");
+    const int64_t logits_rows = n_req * (int64_t)(k + 1);
+    td.row_k = k;
+    td.row_bonus = 0;
+    td.logits_rows = logits_rows;
+    td.stats = draft_stats;
+    tb.row_k = k;
+    tb.row_bonus = 1;
+    tb.logits_rows = logits_rows;
+    tb.stats = bonus_stats;
+    hipError_t e = vpa::launch_block_stats(esize_of(dtype), td, tb, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "vpa_verify_stats launch");
+}
+
+vpa_status vpa_combine_stats(const vpa_stat* stats, int32_t n_shards, int64_t n_rows, int32_t m,
+                             int32_t* ids, uint32_t* val_bits, void* stream) {
+    if (n_shards < 1 || m < 1 || (int64_t)n_shards * m > INT32_MAX)
+        return fail(VPA_ERR_INVALID, "n_shards %d / m %d invalid", (int)n_shards, (int)m);
+    if (n_rows < 0 || n_rows > INT32_MAX)
+        return fail(VPA_ERR_INVALID, "n_rows %lld out of range", (long long)n_rows);
+    if (n_rows == 0)
+        return ok();
+    if (!stats || !aligned(stats, 8))
+        return fail(VPA_ERR_INVALID, "stats is NULL or not 8-byte aligned");
+    if (!ids || !aligned(ids, 4) || (val_bits && !aligned(val_bits, 4)))
+        return fail(VPA_ERR_INVALID, "ids is NULL, or ids/val_bits not 4-byte aligned");
+    hipError_t e = vpa::launch_combine(stats, n_shards, (int32_t)n_rows, m, ids, val_bits,
+                                       (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "vpa_combine_stats launch");
+}
+
+size_t vpa_top_tokens_workspace(vpa_vocab v, int64_t n_rows, int32_t block) {
+    if (n_rows <= 0 || v.vocab < 1 || v.vocab >= VPA_MAX_VOCAB || v.n_shards < 1 ||
+        v.shard_width < 1 || (int64_t)v.n_shards * v.shard_width < v.vocab)
+        return 0;
+    const int64_t m = slots(v.shard_width, v.n_shards, block);
+    if (m < 1)
+        return 0;
+    return (size_t)(v.n_shards * n_rows * m) * sizeof(vpa_stat);
+}
+
+vpa_status vpa_top_tokens(const void* logits, vpa_dtype dtype, int64_t ld, vpa_vocab v,
+                          int64_t n_rows, int32_t block, void* workspace, size_t workspace_bytes,
+                          int32_t* ids, uint32_t* val_bits, void* stream) {
+    vpa::SegTask t;
+    vpa_status st = check_logits_task(logits, dtype, ld, v, 0, v.n_shards, block, t);
+    if (st != VPA_OK)
+        return st;
+    if (n_rows < 0)
+        return fail(VPA_ERR_INVALID, "n_rows %lld < 0", (long long)n_rows);
+    if ((st = set_items(t, n_rows, "vpa_top_tokens")) != VPA_OK)
+        return st;
+    if (n_rows == 0)
+        return ok();
+    if ((st = check_logits_ptr(logits, dtype)) != VPA_OK)
+        return st;
+    const size_t need = vpa_top_tokens_workspace(v, n_rows, block);
+    if (!workspace || !aligned(workspace, 8) || workspace_bytes < need)
+        return fail(VPA_ERR_INVALID, "workspace NULL, unaligned or smaller than %zu bytes", need);
+    if (!ids || !aligned(ids, 4) || (val_bits && !aligned(val_bits, 4)))
+        return fail(VPA_ERR_INVALID, "ids is NULL, or ids/val_bits not 4-byte aligned");
+    t.logits_rows = n_rows;
+    t.stats = (vpa_stat*)workspace;
+    vpa::SegTask none{};
+    hipError_t e = vpa::launch_block_stats(esize_of(dtype), t, none, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "vpa_top_tokens statistics launch");
+    e = vpa::launch_combine(t.stats, v.n_shards, (int32_t)n_rows, t.m, ids, val_bits,
+                            (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "vpa_top_tokens combine launch");
+}
+
+vpa_status vpa_greedy_verify(const vpa_stat* draft_stats, int32_t m_draft,
+                             const vpa_stat* bonus_stats, int32_t m_bonus, int32_t n_shards,
+                             int64_t n_req, int32_t k, const int32_t* draft_ids,
+                             int32_t* out_tokens, int32_t* num_sampled, int32_t* num_rejected,
+                             int32_t* target_ids, void* stream) {
+    if (n_shards < 1 || m_draft < 1 || m_bonus < 1 || (int64_t)n_shards * m_draft > INT32_MAX ||
+        (int64_t)n_shards * m_bonus > INT32_MAX)
+        return fail(VPA_ERR_INVALID, "n_shards %d / m_draft %d / m_bonus %d invalid",
+                    (int)n_shards, (int)m_draft, (int)m_bonus);
+    if (k < 1)
+        return fail(VPA_ERR_INVALID, "k %d < 1", (int)k);
+    if (n_req < 0 || n_req * (int64_t)(k + 1) > INT32_MAX)
+        return fail(VPA_ERR_INVALID, "n_req %lld out of range", (long long)n_req);
+    if (n_req == 0)
+        return ok();
+    if (!draft_stats || !bonus_stats || !aligned(draft_stats, 8) || !aligned(bonus_stats, 8))
+        return fail(VPA_ERR_INVALID, "draft_stats/bonus_stats NULL or not 8-byte aligned");
+    if (!draft_ids || !out_tokens || !num_sampled || !num_rejected)
+        return fail(VPA_ERR_INVALID, "draft_ids/out_tokens/num_sampled/num_rejected is NULL");
+    if (!aligned(draft_ids, 4) || !aligned(out_tokens, 4) || !aligned(num_sampled, 4) ||
+        !aligned(num_rejected, 4) || (target_ids && !aligned(target_ids, 4)))
+        return fail(VPA_ERR_INVALID, "an int32 array is not 4-byte aligned");
+    hipError_t e = vpa::launch_greedy_verify(draft_stats, m_draft, bonus_stats, m_bonus, n_shards,
+                                             (int32_t)n_req, k, draft_ids, out_tokens, num_sampled,
+                                             num_rejected, target_ids, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "vpa_greedy_verify launch");
+}
+
+const char* vpa_last_error(void) {
+    return g_last_error.c_str();
+}
+
+}  // extern "C"

@@ -1,0 +1,140 @@
+// reduce.hip -- the steps after the statistics exchange: rank-order
+// combination into the global argmax, and greedy verification.
+//
+// vLLM PR #34049, "Solution", step 3: a reduction over the gathered
+// (max, global index) pairs gives the global argmax.  vLLM PR #62604,
+// "Purpose" item 1: one kernel finishes the global argmax, the acceptance,
+// the bonus token and the sampled/rejected counts from the gathered per-block
+// statistics.
+//
+// Statistics arrive in rank order, [S][rows][M].  One wavefront handles one
+// row (combine) or one request (verify): lanes stride over the row's S*M
+// statistics, keep the best under the argmax order (key of the value bits,
+// then the lower id), and a shuffle reduction finishes.  The lexicographic
+// (key, -id) maximum is order independent, so the result equals a scan in
+// rank order that keeps only strictly better statistics; an empty slot
+// (-inf, id INT32_MAX) loses to every real statistic.
+#include "vpa_device.h"
+#include "vpa_internal.h"
+
+namespace vpa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
+// Best statistic of row `row` of a [S][rows_total][m] array; every lane
+// returns the same (id, bits).
+__device__ __forceinline__ void row_best(const vpa_stat* __restrict__ stats, int32_t n_shards,
+                                         int64_t rows_total, int64_t row, int32_t m, int lane,
+                                         int32_t& id, uint32_t& bits) {
+    uint32_t bk = 0, bn = 0, bb = 0;
+    const int32_t total = n_shards * m;
+    for (int32_t idx = lane; idx < total; idx += 64) {
+        const int32_t s = idx / m;
+        const int32_t j = idx - s * m;
+        const vpa_stat st = stats[((int64_t)s * rows_total + row) * m + j];
+        const uint32_t k = key_f32(st.val_bits);
+        const uint32_t n = ~(uint32_t)st.id;
+        if (k > bk || (k == bk && n > bn)) {
+            bk = k;
+            bn = n;
+            bb = st.val_bits;
+        }
+    }
+    wave_best_stat(bk, bn, bb);
+    id = (int32_t)~bn;
+    bits = bb;
+}
+
+__global__ __launch_bounds__(kThreads) void combine_kernel(const vpa_stat* __restrict__ stats,
+                                                           int32_t n_shards, int32_t n_rows,
+                                                           int32_t m, int32_t* __restrict__ ids,
+                                                           uint32_t* __restrict__ val_bits) {
+    const int lane = threadIdx.x & 63;
+    const int32_t wave = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
+    const int32_t row = (int32_t)blockIdx.x * kWaves + wave;
+    if (row >= n_rows)
+        return;
+    int32_t id;
+    uint32_t bits;
+    row_best(stats, n_shards, n_rows, row, m, lane, id, bits);
+    if (lane == 0) {
+        ids[row] = id;
+        if (val_bits)
+            val_bits[row] = bits;
+    }
+}
+
+// Request r: target token of draft position j is the best statistic of row
+// r*K+j of draft_stats, that of the bonus position the best of row r of
+// bonus_stats.  Drafts are accepted while they equal their target; the first
+// differing position (or position K) emits its target; later positions -1.
+__global__ __launch_bounds__(kThreads) void greedy_verify_kernel(
+    const vpa_stat* __restrict__ draft_stats, int32_t m_draft,
+    const vpa_stat* __restrict__ bonus_stats, int32_t m_bonus, int32_t n_shards, int32_t n_req,
+    int32_t k, const int32_t* __restrict__ draft_ids, int32_t* __restrict__ out_tokens,
+    int32_t* __restrict__ num_sampled, int32_t* __restrict__ num_rejected,
+    int32_t* __restrict__ target_ids) {
+    const int lane = threadIdx.x & 63;
+    const int32_t wave = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
+    const int32_t r = (int32_t)blockIdx.x * kWaves + wave;
+    if (r >= n_req)
+        return;
+    const int64_t base = (int64_t)r * (k + 1);
+    int32_t accepted = -1;   // set at the first position that emits its target
+    for (int32_t j = 0; j <= k; ++j) {
+        if (accepted >= 0 && !target_ids) {
+            if (lane == 0)
+                out_tokens[base + j] = -1;
+            continue;
+        }
+        int32_t tgt;
+        uint32_t bits;
+        if (j < k)
+            row_best(draft_stats, n_shards, (int64_t)n_req * k, (int64_t)r * k + j, m_draft, lane,
+                     tgt, bits);
+        else
+            row_best(bonus_stats, n_shards, n_req, r, m_bonus, lane, tgt, bits);
+        int32_t tok = -1;
+        if (accepted < 0) {
+            const int32_t d = j < k ? draft_ids[(int64_t)r * k + j] : -1;
+            tok = tgt;
+            if (j == k || d != tgt)
+                accepted = j;
+        }
+        if (lane == 0) {
+            out_tokens[base + j] = tok;
+            if (target_ids)
+                target_ids[base + j] = tgt;
+        }
+    }
+    if (lane == 0) {
+        num_sampled[r] = accepted + 1;
+        num_rejected[r] = k - accepted;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const vpa_stat* stats, int32_t n_shards, int32_t n_rows, int32_t m,
+                          int32_t* ids, uint32_t* val_bits, hipStream_t stream) {
+    const dim3 grid((unsigned)((n_rows + kWaves - 1) / kWaves));
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(kThreads), 0, stream, stats, n_shards, n_rows, m,
+                       ids, val_bits);
+    return hipGetLastError();
+}
+
+hipError_t launch_greedy_verify(const vpa_stat* draft_stats, int32_t m_draft,
+                                const vpa_stat* bonus_stats, int32_t m_bonus, int32_t n_shards,
+                                int32_t n_req, int32_t k, const int32_t* draft_ids,
+                                int32_t* out_tokens, int32_t* num_sampled, int32_t* num_rejected,
+                                int32_t* target_ids, hipStream_t stream) {
+    const dim3 grid((unsigned)((n_req + kWaves - 1) / kWaves));
+    hipLaunchKernelGGL(greedy_verify_kernel, grid, dim3(kThreads), 0, stream, draft_stats, m_draft,
+                       bonus_stats, m_bonus, n_shards, n_req, k, draft_ids, out_tokens,
+                       num_sampled, num_rejected, target_ids);
+    return hipGetLastError();
+}
+
+}  // namespace vpa

@@ -1,0 +1,48 @@
+// vpa_internal.h -- declarations shared by the HIP sources of libvpa (not
+// part of the public C ABI, which is include/vpa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "vpa.h"
+
+namespace vpa {
+
+// One launch's worth of (row, shard, slot) work items for the block-statistics
+// kernel.  Item t decodes as row i = t / (n_local*m), local shard
+// sl = (t / m) % n_local, slot j = t % m; consecutive items therefore walk a
+// row's columns in ascending order.
+struct SegTask {
+    const unsigned char* base;  // logits, column 0 = global column col0
+    int64_t ld;                 // row stride, elements
+    int64_t vocab;              // V
+    int64_t shard_width;        // W
+    int64_t col0;               // first_shard * W
+    int64_t logits_rows;        // rows[] entries must lie in [0, logits_rows)
+    const int32_t* rows;        // row list or nullptr
+    vpa_stat* stats;            // [n_local][n_rows][m]
+    int32_t n_rows;
+    int32_t n_items;            // n_rows * n_local * m (< 2^31, checked by the host)
+    int32_t first_shard;
+    int32_t n_local;
+    int32_t block;
+    int32_t m;
+    int32_t row_k;              // > 0: verification rows with K = row_k (rows ignored)
+    int32_t row_bonus;          // with row_k > 0: 1 = bonus rows, 0 = draft rows
+};
+
+// Launch the block-statistics kernel over the items of t0 followed by those
+// of t1 (t1.n_items may be 0).  Both tasks share dtype `esize` (2 or 4).
+hipError_t launch_block_stats(int esize, const SegTask& t0, const SegTask& t1, hipStream_t stream);
+
+hipError_t launch_combine(const vpa_stat* stats, int32_t n_shards, int32_t n_rows, int32_t m,
+                          int32_t* ids, uint32_t* val_bits, hipStream_t stream);
+
+hipError_t launch_greedy_verify(const vpa_stat* draft_stats, int32_t m_draft,
+                                const vpa_stat* bonus_stats, int32_t m_bonus, int32_t n_shards,
+                                int32_t n_req, int32_t k, const int32_t* draft_ids,
+                                int32_t* out_tokens, int32_t* num_sampled, int32_t* num_rejected,
+                                int32_t* target_ids, hipStream_t stream);
+
+}  // namespace vpa
