@@ -83,6 +83,7 @@ typedef struct {
 #define VPA_EMPTY_BITS 0xFF800000u
 #define VPA_EMPTY_ID 0x7FFFFFFF
 #define VPA_MAX_VOCAB (1 << 24) /* the vocabulary must stay below this */
+#define VPA_MAX_DRAFTS 4096     /* most draft tokens per request (K) */
 
 /* Vocabulary geometry: V valid columns, S shards of W columns each. */
 typedef struct {
@@ -127,7 +128,7 @@ vpa_status vpa_block_stats(const void* logits, vpa_dtype dtype, int64_t ld, vpa_
  *  draft_stats  out, [n_local_shards][n_req*K][M_draft], row r*K+j is draft
  *               position j of request r; M_draft = vpa_stats_slots(W,S,block_draft).
  *  bonus_stats  out, [n_local_shards][n_req][M_bonus]; M_bonus likewise.
- * Other arguments as vpa_block_stats; k >= 1. */
+ * Other arguments as vpa_block_stats; 1 <= k <= VPA_MAX_DRAFTS. */
 vpa_status vpa_verify_stats(const void* logits, vpa_dtype dtype, int64_t ld, vpa_vocab v,
                             int32_t first_shard, int32_t n_local_shards, int64_t n_req, int32_t k,
                             int32_t block_draft, int32_t block_bonus, vpa_stat* draft_stats,
@@ -172,7 +173,8 @@ vpa_status vpa_top_tokens(const void* logits, vpa_dtype dtype, int64_t ld, vpa_v
  *  num_sampled  out, int32 [n_req]: accepted + 1.
  *  num_rejected out, int32 [n_req]: K - accepted.
  *  target_ids   out, int32 [n_req][K+1], or NULL: the target token of every
- *               position. */
+ *               position.
+ *  1 <= k <= VPA_MAX_DRAFTS. */
 vpa_status vpa_greedy_verify(const vpa_stat* draft_stats, int32_t m_draft,
                              const vpa_stat* bonus_stats, int32_t m_bonus, int32_t n_shards,
                              int64_t n_req, int32_t k, const int32_t* draft_ids,

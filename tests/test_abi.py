@@ -147,7 +147,10 @@ def test_verify_rejects(lib):
                                 FAKE, None) == vpa.VPA_ERR_INVALID
     assert lib.vpa_verify_stats(FAKE, vpa.VPA_BF16, 200064, voc, 0, 4, 24, 3, 8192, 1024, None,
                                 FAKE, None) == vpa.VPA_ERR_INVALID
+    assert lib.vpa_verify_stats(FAKE, vpa.VPA_BF16, 200064, voc, 0, 4, 24, 4097, 8192, 1024, FAKE,
+                                FAKE, None) == vpa.VPA_ERR_INVALID
     gv = lib.vpa_greedy_verify
+    assert gv(FAKE, 7, FAKE, 50, 4, 24, 4097, FAKE, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
     assert gv(FAKE, 7, FAKE, 50, 4, 24, 0, FAKE, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
     assert gv(FAKE, 0, FAKE, 50, 4, 24, 3, FAKE, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
     assert gv(FAKE, 7, FAKE, 50, 0, 24, 3, FAKE, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID

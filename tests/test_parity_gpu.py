@@ -109,6 +109,25 @@ def test_edge_verify(case):
                 _verify_both(x, v, w, s, n_req, k, drafts, bd, bb, case.name)
 
 
+@pytest.mark.parametrize("k", [2, 16, 17, 40])
+def test_verify_many_drafts(k):
+    """K beyond one wavefront per position (more positions than waves in the
+    finishing workgroup), random plans including placeholders."""
+    vocab, s = 1000, 3
+    w = -(-vocab // s)
+    n_req = 9
+    g = torch.Generator().manual_seed(4000 + k)
+    x = (torch.randn((n_req * (k + 1), s * w), generator=g) * 2).to(torch.bfloat16)
+    x[:, vocab:] = float("nan")
+    tgt, _ = oracle.argmax(x, vocab)
+    plan = torch.where(torch.rand((n_req, k), generator=g) < 0.9, 1, 0).to(torch.int8)
+    plan[0, k // 2:] = -1
+    plan[1, :] = 1
+    uniform = torch.randint(0, vocab, (n_req, k), generator=g, dtype=torch.int64).to(torch.int32)
+    drafts = workloads.compose_drafts(tgt.reshape(n_req, k + 1), plan, uniform)
+    _verify_both(x, vocab, w, s, n_req, k, drafts, 256, 64, f"many drafts K={k}")
+
+
 def test_row_list_out_of_range_rows_are_empty():
     case = workloads.edge_cases()[3]                      # vocab 1000, 8 shards, bf16
     x = _dev(case.logits)

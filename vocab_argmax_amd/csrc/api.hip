@@ -178,8 +178,8 @@ vpa_status vpa_verify_stats(const void* logits, vpa_dtype dtype, int64_t ld, vpa
     if ((st = check_logits_task(logits, dtype, ld, v, first_shard, n_local_shards, block_bonus,
                                 tb)) != VPA_OK)
         return st;
-    if (k < 1)
-        return fail(VPA_ERR_INVALID, "k %d < 1", (int)k);
+    if (k < 1 || k > VPA_MAX_DRAFTS)
+        return fail(VPA_ERR_INVALID, "k %d outside [1, %d]", (int)k, VPA_MAX_DRAFTS);
     if (n_req < 0 || n_req * (int64_t)(k + 1) > INT32_MAX)
         return fail(VPA_ERR_INVALID, "n_req %lld out of range", (long long)n_req);
     if ((st = set_items(td, n_req * k, "vpa_verify_stats (draft rows)")) != VPA_OK)
@@ -274,8 +274,8 @@ vpa_status vpa_greedy_verify(const vpa_stat* draft_stats, int32_t m_draft,
         (int64_t)n_shards * m_bonus > INT32_MAX)
         return fail(VPA_ERR_INVALID, "n_shards %d / m_draft %d / m_bonus %d invalid",
                     (int)n_shards, (int)m_draft, (int)m_bonus);
-    if (k < 1)
-        return fail(VPA_ERR_INVALID, "k %d < 1", (int)k);
+    if (k < 1 || k > VPA_MAX_DRAFTS)
+        return fail(VPA_ERR_INVALID, "k %d outside [1, %d]", (int)k, VPA_MAX_DRAFTS);
     if (n_req < 0 || n_req * (int64_t)(k + 1) > INT32_MAX)
         return fail(VPA_ERR_INVALID, "n_req %lld out of range", (long long)n_req);
     if (n_req == 0)

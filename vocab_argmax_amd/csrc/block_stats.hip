@@ -7,13 +7,16 @@
 // item 2: padding columns are masked.  Here a "segment" is one statistic's
 // column range: block b = floor(s*W/B) + j cut to shard s and to [0, V).
 //
-// Work decomposition (CDNA4, wave64): one wavefront per segment, four
-// wavefronts per workgroup, no LDS and no barriers.  A wave streams its
-// segment with 16-byte non-temporal loads (one 1 KiB wave-wide load per
-// iteration, up to 16 iterations -- 16 KiB -- in flight per wave), keeps a
-// running best per lane, and finishes with a shuffle reduction.  Segments of
-// a row are consecutive work items, so consecutive waves read consecutive
-// memory.  Padding columns [V, S*W) are never read.
+// Work decomposition (CDNA4, wave64): a segment is scanned by a group of L
+// lanes of one wavefront (L = 64 for 8192-column bf16 blocks, down to 8 for
+// 1024-column ones), so a lane makes about 16 iterations of 16-byte
+// non-temporal loads whatever the block size, issued 8 at a time (8 KiB per
+// wavefront in flight); four wavefronts per workgroup, no LDS and no
+// barriers.  Chunks of 8 keep the kernel under 70 VGPRs, i.e. 7 wavefronts
+// per SIMD, which measured faster on MI355X than 16-deep chunks at 4.  Each lane keeps a running best, and a
+// shuffle reduction inside the group finishes the segment.  Consecutive
+// groups and wavefronts take consecutive segments of a row, so a wavefront
+// reads contiguous memory.  Padding columns [V, S*W) are never read.
 //
 // Per-lane scan.  Every element becomes an order-preserving unsigned key
 // (vpa_device.h); bf16 keys are 16 bits wide and computed two at a time with
@@ -21,22 +24,36 @@
 // position) with one unsigned max: the largest key wins and, among equal
 // keys, the earliest position.  For fp32 a strict greater-than keeps the
 // first of equal keys.  The winning position decodes back to a global
-// column; the wave then takes the lexicographic maximum of (key, -column),
+// column; the group then takes the lexicographic maximum of (key, -column),
 // which is associative and commutative, so any lane layout or chunking gives
 // the same statistic.
 //
 // Alignment.  Rows may start at any element-aligned address (an unaligned
 // vocabulary padding makes odd row strides).  The segment's full 16-byte
 // vectors are streamed; the at most 2*(16/esize - 1) elements before the
-// first and after the last full vector are read one by one by lanes 0..31.
+// first and after the last full vector are read one by one.
 #include "vpa_device.h"
 #include "vpa_internal.h"
 
 namespace vpa {
 namespace {
 
-constexpr int kWaves = 4;
+#ifndef VPA_WAVES_PER_WG
+#define VPA_WAVES_PER_WG 4
+#endif
+#ifndef VPA_ITERS_PER_CHUNK
+#define VPA_ITERS_PER_CHUNK 8
+#endif
+#ifndef VPA_NT_LOADS
+#define VPA_NT_LOADS 1
+#endif
+#ifndef VPA_LANE_ITERS
+#define VPA_LANE_ITERS 16
+#endif
+constexpr int kWaves = VPA_WAVES_PER_WG;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kItersPerChunk = VPA_ITERS_PER_CHUNK;   // group iterations loaded together
+constexpr int kLaneIters = VPA_LANE_ITERS;   // target iterations per lane of a segment
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef const u32x4 __attribute__((address_space(1)))* gvec_ptr;
@@ -50,21 +67,25 @@ __device__ __forceinline__ void take_better(uint32_t& bk, int32_t& bc, uint32_t 
     }
 }
 
-// One chunk of U wave iterations over the segment's full vectors seg[0, n):
-// lane reads seg[i0 + 64*u] for u < U, with i0 = lane + 64*t0.  FULL: every
-// such index is below n; otherwise indices are clamped to n-1, which only
-// re-reads that vector (a duplicate decodes to the same column, so it cannot
-// change the result).  Column of element e of seg[i] = c0 + i*VEC + e.
-template <int ESIZE, int U, bool FULL>
+// One chunk of U group iterations over the segment's full vectors seg[0, n):
+// the lane reads seg[i0 + L*u] for u < U, with i0 = (lane in group) + L*t0.
+// FULL: every such index is below n; otherwise indices are clamped to n-1,
+// which only re-reads that vector (a duplicate decodes to the same column, so
+// it cannot change the result).  Column of element e of seg[i] = c0 + i*VEC + e.
+template <int ESIZE, int L, int U, bool FULL>
 __device__ __forceinline__ void scan_chunk(gvec_ptr seg, uint32_t i0, uint32_t ilast, int32_t c0,
                                            uint32_t& bk, int32_t& bc) {
     u32x4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        uint32_t i = i0 + 64 * u;
+        uint32_t i = i0 + L * u;
         if (!FULL)
             i = i < ilast ? i : ilast;
+#if VPA_NT_LOADS
         v[u] = __builtin_nontemporal_load(seg + i);
+#else
+        v[u] = seg[i];
+#endif
     }
     if constexpr (ESIZE == 2) {
         // key16 << 16 | (0xFFFF - position): one unsigned max keeps the largest
@@ -84,7 +105,7 @@ __device__ __forceinline__ void scan_chunk(gvec_ptr seg, uint32_t i0, uint32_t i
             }
         }
         const uint32_t pos = 0xFFFFu - (best & 0xFFFFu);
-        uint32_t i = i0 + 64 * (pos >> 3);
+        uint32_t i = i0 + L * (pos >> 3);
         if (!FULL)
             i = i < ilast ? i : ilast;
         take_better(bk, bc, best >> 16, c0 + (int32_t)(i * 8 + (pos & 7)));
@@ -101,36 +122,55 @@ __device__ __forceinline__ void scan_chunk(gvec_ptr seg, uint32_t i0, uint32_t i
                 }
             }
         }
-        uint32_t i = i0 + 64 * (cpos >> 2);
+        uint32_t i = i0 + L * (cpos >> 2);
         if (!FULL)
             i = i < ilast ? i : ilast;
         take_better(bk, bc, ck, c0 + (int32_t)(i * 4 + (cpos & 3)));
     }
 }
 
-template <int ESIZE, int U>
-__device__ __forceinline__ void scan_iters(gvec_ptr seg, uint32_t n, uint32_t t0, int lane,
+// Iterations [t0, t0+U) of the group.  The unclamped form is used only when
+// it is valid for every group of the wavefront, so the branch is uniform.
+template <int ESIZE, int L, int U>
+__device__ __forceinline__ void scan_iters(gvec_ptr seg, uint32_t n, uint32_t t0, uint32_t gl,
                                            int32_t c0, uint32_t& bk, int32_t& bc) {
-    const uint32_t i0 = (uint32_t)lane + 64 * t0;
-    if (64 * (t0 + U) <= n)
-        scan_chunk<ESIZE, U, true>(seg, i0, n - 1, c0, bk, bc);
+    const uint32_t i0 = gl + L * t0;
+    if (__all(L * (t0 + U) <= n))
+        scan_chunk<ESIZE, L, U, true>(seg, i0, n - 1, c0, bk, bc);
     else
-        scan_chunk<ESIZE, U, false>(seg, i0, n - 1, c0, bk, bc);
+        scan_chunk<ESIZE, L, U, false>(seg, i0, n - 1, c0, bk, bc);
 }
 
 __device__ __forceinline__ uint32_t load_bits(const unsigned char* base, int esize, int64_t e) {
     return esize == 2 ? (uint32_t)((gu16_ptr)base)[e] << 16 : ((gu32_ptr)base)[e];
 }
 
-template <int ESIZE>
-__device__ void segment_stat(const SegTask& t, int32_t item, int lane) {
+// Group-wide lexicographic maximum of (key, -column) over aligned groups of
+// L lanes (L a power of two <= 64).
+template <int L>
+__device__ __forceinline__ void group_best_key_col(uint32_t& key, int32_t& col) {
+#pragma unroll
+    for (int off = L >> 1; off >= 1; off >>= 1) {
+        const uint32_t ok = __shfl_xor(key, (int)off, 64);
+        const int32_t oc = __shfl_xor(col, (int)off, 64);
+        take_better(key, col, ok, oc);
+    }
+}
+
+// The statistic of item `item` of task t, computed by the L lanes of the
+// group (this lane is lane `gl` of it; with L = 64 the item is uniform).
+// Every lane of the wavefront reaches the reduction (no early return), so the
+// shuffles read live lanes only.
+template <int ESIZE, int L>
+__device__ __forceinline__ void segment_stat(const SegTask& t, int32_t item, uint32_t gl) {
     constexpr int VEC = 16 / ESIZE;
+    const bool live = item < t.n_items;
+    const int32_t it = live ? item : 0;
     const int32_t m = t.m;
-    const int32_t j = item % m;
-    const int32_t rest = item / m;
+    const int32_t j = it % m;
+    const int32_t rest = it / m;
     const int32_t sl = rest % t.n_local;
     const int32_t i = rest / t.n_local;
-    vpa_stat* out = t.stats + ((int64_t)sl * t.n_rows + i) * m + j;
 
     int64_t row;
     if (t.row_k > 0) {
@@ -145,107 +185,149 @@ __device__ void segment_stat(const SegTask& t, int32_t item, int lane) {
     int64_t hi = blo + t.block;
     hi = hi < shard_lo + t.shard_width ? hi : shard_lo + t.shard_width;
     hi = hi < t.vocab ? hi : t.vocab;
-    if (lo >= hi || row < 0 || row >= t.logits_rows) {
-        if (lane == 0) {
-            vpa_stat e;
-            e.val_bits = VPA_EMPTY_BITS;
-            e.id = VPA_EMPTY_ID;
-            *out = e;
-        }
-        return;
-    }
-
-    // Aligned element index a = buffer element index + mis, so that vector q
-    // holds aligned indices [q*VEC, (q+1)*VEC); column = a + D.
-    const uintptr_t base = (uintptr_t)t.base;
-    const int64_t mis = (int64_t)(base & 15) / ESIZE;
-    const int64_t a_lo = row * t.ld + (lo - t.col0) + mis;
-    const int64_t D = lo - a_lo;
-    const int64_t qa = (a_lo + VEC - 1) / VEC;
-    int64_t qb = (a_lo + (hi - lo)) / VEC;
-    int64_t head_end, tail_lo;
-    if (qa < qb) {
-        head_end = qa * VEC + D;
-        tail_lo = qb * VEC + D;
-    } else {
-        head_end = hi;
-        tail_lo = hi;
-        qb = qa;
-    }
-    // The segment's full vectors, seg[0, n); a segment is at most 2^24
-    // elements, so 32-bit offsets suffice.
-    const gvec_ptr seg = (gvec_ptr)(base - (uintptr_t)(mis * ESIZE)) + qa;
-    const uint32_t n = (uint32_t)(qb - qa);
-    const int32_t c0 = (int32_t)(qa * VEC + D);
+    const bool work = live && lo < hi && row >= 0 && row < t.logits_rows;
 
     uint32_t bk = 0;
     int32_t bc = INT32_MAX;
-    {
-        const int64_t c = lane < 16 ? lo + lane : tail_lo + (lane - 16);
-        const bool has = lane < 16 ? c < head_end : (lane < 32 && c < hi);
-        if (has) {
-            const uint32_t f = load_bits(t.base, ESIZE, row * t.ld + (c - t.col0));
-            bk = ESIZE == 2 ? key_bf16(f >> 16) : key_f32(f);
-            bc = (int32_t)c;
+    if (work) {
+        // Aligned element index a = buffer element index + mis, so that
+        // vector q holds aligned indices [q*VEC, (q+1)*VEC); column = a + D.
+        const uintptr_t base = (uintptr_t)t.base;
+        const int64_t mis = (int64_t)(base & 15) / ESIZE;
+        const int64_t a_lo = row * t.ld + (lo - t.col0) + mis;
+        const int64_t D = lo - a_lo;
+        const int64_t qa = (a_lo + VEC - 1) / VEC;
+        int64_t qb = (a_lo + (hi - lo)) / VEC;
+        int64_t head_end, tail_lo;
+        if (qa < qb) {
+            head_end = qa * VEC + D;
+            tail_lo = qb * VEC + D;
+        } else {
+            head_end = hi;
+            tail_lo = hi;
+            qb = qa;
         }
+        // Edge elements, one by one (at most 2*(VEC-1) of them).
+        for (int64_t c = lo + gl; c < head_end; c += L) {
+            const uint32_t f = load_bits(t.base, ESIZE, row * t.ld + (c - t.col0));
+            take_better(bk, bc, ESIZE == 2 ? key_bf16(f >> 16) : key_f32(f), (int32_t)c);
+        }
+        for (int64_t c = tail_lo + gl; c < hi; c += L) {
+            const uint32_t f = load_bits(t.base, ESIZE, row * t.ld + (c - t.col0));
+            take_better(bk, bc, ESIZE == 2 ? key_bf16(f >> 16) : key_f32(f), (int32_t)c);
+        }
+        // The segment's full vectors, seg[0, n); a segment is at most 2^24
+        // elements, so 32-bit offsets suffice.
+        const gvec_ptr seg = (gvec_ptr)(base - (uintptr_t)(mis * ESIZE)) + qa;
+        const uint32_t n = (uint32_t)(qb - qa);
+        const int32_t c0 = (int32_t)(qa * VEC + D);
+        const uint32_t nit = (n + L - 1) / L;   // group iterations over full vectors
+        uint32_t t0 = 0;
+        for (; t0 + kItersPerChunk <= nit; t0 += kItersPerChunk)
+            scan_iters<ESIZE, L, kItersPerChunk>(seg, n, t0, gl, c0, bk, bc);
+        if (t0 + 8 <= nit) {
+            scan_iters<ESIZE, L, 8>(seg, n, t0, gl, c0, bk, bc);
+            t0 += 8;
+        }
+        if (t0 + 4 <= nit) {
+            scan_iters<ESIZE, L, 4>(seg, n, t0, gl, c0, bk, bc);
+            t0 += 4;
+        }
+        if (t0 + 2 <= nit) {
+            scan_iters<ESIZE, L, 2>(seg, n, t0, gl, c0, bk, bc);
+            t0 += 2;
+        }
+        if (t0 < nit)
+            scan_iters<ESIZE, L, 1>(seg, n, t0, gl, c0, bk, bc);
     }
 
-    const uint32_t nit = (n + 63) >> 6;   // wave iterations over full vectors
-    uint32_t t0 = 0;
-    for (; t0 + 16 <= nit; t0 += 16)
-        scan_iters<ESIZE, 16>(seg, n, t0, lane, c0, bk, bc);
-    if (t0 + 8 <= nit) {
-        scan_iters<ESIZE, 8>(seg, n, t0, lane, c0, bk, bc);
-        t0 += 8;
-    }
-    if (t0 + 4 <= nit) {
-        scan_iters<ESIZE, 4>(seg, n, t0, lane, c0, bk, bc);
-        t0 += 4;
-    }
-    if (t0 + 2 <= nit) {
-        scan_iters<ESIZE, 2>(seg, n, t0, lane, c0, bk, bc);
-        t0 += 2;
-    }
-    if (t0 < nit)
-        scan_iters<ESIZE, 1>(seg, n, t0, lane, c0, bk, bc);
+    group_best_key_col<L>(bk, bc);
 
-    wave_best_key_col(bk, bc);
-
-    uint32_t bits;
-    if (ESIZE == 2 ? (bk == kKeyNanBf16 || bk == kKeyZeroBf16)
-                   : (bk == kKeyNanF32 || bk == kKeyZeroF32))
-        bits = load_bits(t.base, ESIZE, row * t.ld + ((int64_t)bc - t.col0));
-    else
-        bits = ESIZE == 2 ? bits_of_key_bf16(bk) : bits_of_key_f32(bk);
-    if (lane == 0) {
+    if (gl == 0 && live) {
         vpa_stat st;
-        st.val_bits = bits;
-        st.id = bc;
-        *out = st;
+        if (!work) {
+            st.val_bits = VPA_EMPTY_BITS;
+            st.id = VPA_EMPTY_ID;
+        } else {
+            const bool reread = ESIZE == 2 ? (bk == kKeyNanBf16 || bk == kKeyZeroBf16)
+                                           : (bk == kKeyNanF32 || bk == kKeyZeroF32);
+            st.val_bits = reread ? load_bits(t.base, ESIZE, row * t.ld + ((int64_t)bc - t.col0))
+                                 : (ESIZE == 2 ? bits_of_key_bf16(bk) : bits_of_key_f32(bk));
+            st.id = bc;
+        }
+        t.stats[((int64_t)sl * t.n_rows + i) * m + j] = st;
+    }
+}
+
+// Task t's items for this wavefront, with groups of 2^LG lanes.
+template <int ESIZE, int LG>
+__device__ __forceinline__ void wave_items(const SegTask& t, int32_t wave, uint32_t lane) {
+    const int32_t item = (wave << (6 - LG)) + (int32_t)(lane >> LG);
+    segment_stat<ESIZE, 1 << LG>(t, item, lane & ((1u << LG) - 1));
+}
+
+template <int ESIZE>
+__device__ __forceinline__ void task_wave(const SegTask& t, int32_t wave, uint32_t lane) {
+    switch (t.lanes_log2) {   // uniform: a kernel argument
+    case 6:
+        wave_items<ESIZE, 6>(t, wave, lane);
+        break;
+    case 5:
+        wave_items<ESIZE, 5>(t, wave, lane);
+        break;
+    case 4:
+        wave_items<ESIZE, 4>(t, wave, lane);
+        break;
+    default:
+        wave_items<ESIZE, 3>(t, wave, lane);
+        break;
     }
 }
 
 template <int ESIZE>
-__global__ __launch_bounds__(kThreads) void block_stats_kernel(SegTask t0, SegTask t1) {
-    const int lane = threadIdx.x & 63;
-    const int32_t wave = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
-    int32_t item = (int32_t)blockIdx.x * kWaves + wave;
-    if (item < t0.n_items) {
-        segment_stat<ESIZE>(t0, item, lane);
+__global__ __launch_bounds__(kThreads)
+#ifdef VPA_WAVES_PER_EU
+__attribute__((amdgpu_waves_per_eu(VPA_WAVES_PER_EU)))
+#endif
+void block_stats_kernel(SegTask t0, SegTask t1) {
+    const uint32_t lane = threadIdx.x & 63;
+    int32_t wave = (int32_t)blockIdx.x * kWaves +
+                   __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
+    if (wave < t0.n_waves) {
+        task_wave<ESIZE>(t0, wave, lane);
         return;
     }
-    item -= t0.n_items;
-    if (item < t1.n_items)
-        segment_stat<ESIZE>(t1, item, lane);
+    wave -= t0.n_waves;
+    if (wave < t1.n_waves)
+        task_wave<ESIZE>(t1, wave, lane);
+}
+
+// Lanes per segment: about kItersPerChunk 16-byte vectors per lane for the
+// longest segment, between 8 lanes (128 contiguous bytes per group load) and
+// the full wavefront.
+int lanes_log2_for(const SegTask& t, int esize) {
+    const int64_t span = t.block < t.shard_width ? t.block : t.shard_width;
+    const int64_t vectors = (span * esize + 15) / 16 + 1;
+    int lg = 3;
+    while (lg < 6 && ((int64_t)1 << (lg + 1)) * kLaneIters <= vectors)
+        ++lg;
+    return lg;
 }
 
 }  // namespace
 
-hipError_t launch_block_stats(int esize, const SegTask& t0, const SegTask& t1, hipStream_t stream) {
-    const int64_t items = (int64_t)t0.n_items + t1.n_items;
-    if (items <= 0)
+hipError_t launch_block_stats(int esize, const SegTask& t0_in, const SegTask& t1_in,
+                              hipStream_t stream) {
+    SegTask t0 = t0_in, t1 = t1_in;
+    for (SegTask* t : {&t0, &t1}) {
+        t->lanes_log2 = lanes_log2_for(*t, esize);
+        const int32_t per_wave = 1 << (6 - t->lanes_log2);
+        t->n_waves = t->n_items > 0 ? (t->n_items + per_wave - 1) / per_wave : 0;
+    }
+    const int64_t waves = (int64_t)t0.n_waves + t1.n_waves;
+    if (waves <= 0)
         return hipSuccess;
-    const dim3 grid((unsigned)((items + kWaves - 1) / kWaves));
+    const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves));
     const dim3 block(kThreads);
     if (esize == 2)
         hipLaunchKernelGGL(block_stats_kernel<2>, grid, block, 0, stream, t0, t1);

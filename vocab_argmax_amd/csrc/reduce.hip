@@ -7,10 +7,10 @@
 // the bonus token and the sampled/rejected counts from the gathered per-block
 // statistics.
 //
-// Statistics arrive in rank order, [S][rows][M].  One wavefront handles one
-// row (combine) or one request (verify): lanes stride over the row's S*M
-// statistics, keep the best under the argmax order (key of the value bits,
-// then the lower id), and a shuffle reduction finishes.  The lexicographic
+// Statistics arrive in rank order, [S][rows][M].  One wavefront reduces one
+// row (a combine row, or one position of a verified request): lanes stride
+// over the row's S*M statistics, keep the best under the argmax order (key of
+// the value bits, then the lower id), and a shuffle reduction finishes.  The lexicographic
 // (key, -id) maximum is order independent, so the result equals a scan in
 // rank order that keeps only strictly better statistics; an empty slot
 // (-inf, id INT32_MAX) loses to every real statistic.
@@ -22,6 +22,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kVerifyMaxThreads = 1024;
 
 // Best statistic of row `row` of a [S][rows_total][m] array; every lane
 // returns the same (id, bits).
@@ -66,29 +67,26 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const vpa_stat* __res
     }
 }
 
-// Request r: target token of draft position j is the best statistic of row
-// r*K+j of draft_stats, that of the bonus position the best of row r of
-// bonus_stats.  Drafts are accepted while they equal their target; the first
-// differing position (or position K) emits its target; later positions -1.
-__global__ __launch_bounds__(kThreads) void greedy_verify_kernel(
+// One workgroup per request r.  Its wavefronts share out the K+1 positions
+// (wave w takes positions w, w + nw, ...): the target token of draft position
+// j is the best statistic of row r*K+j of draft_stats, that of the bonus
+// position the best of row r of bonus_stats.  The targets meet in LDS; after
+// the barrier one lane applies the greedy acceptance: drafts are accepted
+// while they equal their target, the first differing position (or position
+// K) emits its target, later positions hold -1.
+__global__ __launch_bounds__(kVerifyMaxThreads) void greedy_verify_kernel(
     const vpa_stat* __restrict__ draft_stats, int32_t m_draft,
     const vpa_stat* __restrict__ bonus_stats, int32_t m_bonus, int32_t n_shards, int32_t n_req,
     int32_t k, const int32_t* __restrict__ draft_ids, int32_t* __restrict__ out_tokens,
     int32_t* __restrict__ num_sampled, int32_t* __restrict__ num_rejected,
     int32_t* __restrict__ target_ids) {
+    extern __shared__ int32_t targets[];   // k + 1 entries
     const int lane = threadIdx.x & 63;
     const int32_t wave = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
-    const int32_t r = (int32_t)blockIdx.x * kWaves + wave;
-    if (r >= n_req)
-        return;
+    const int32_t n_waves = (int32_t)(blockDim.x >> 6);
+    const int32_t r = (int32_t)blockIdx.x;
     const int64_t base = (int64_t)r * (k + 1);
-    int32_t accepted = -1;   // set at the first position that emits its target
-    for (int32_t j = 0; j <= k; ++j) {
-        if (accepted >= 0 && !target_ids) {
-            if (lane == 0)
-                out_tokens[base + j] = -1;
-            continue;
-        }
+    for (int32_t j = wave; j <= k; j += n_waves) {
         int32_t tgt;
         uint32_t bits;
         if (j < k)
@@ -96,22 +94,22 @@ __global__ __launch_bounds__(kThreads) void greedy_verify_kernel(
                      tgt, bits);
         else
             row_best(bonus_stats, n_shards, n_req, r, m_bonus, lane, tgt, bits);
-        int32_t tok = -1;
-        if (accepted < 0) {
-            const int32_t d = j < k ? draft_ids[(int64_t)r * k + j] : -1;
-            tok = tgt;
-            if (j == k || d != tgt)
-                accepted = j;
-        }
         if (lane == 0) {
-            out_tokens[base + j] = tok;
+            targets[j] = tgt;
             if (target_ids)
                 target_ids[base + j] = tgt;
         }
     }
-    if (lane == 0) {
-        num_sampled[r] = accepted + 1;
-        num_rejected[r] = k - accepted;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int32_t* drafts = draft_ids + (int64_t)r * k;
+        int32_t n = 0;
+        while (n < k && drafts[n] == targets[n])
+            ++n;
+        for (int32_t j = 0; j <= k; ++j)
+            out_tokens[base + j] = j < n ? drafts[j] : (j == n ? targets[j] : -1);
+        num_sampled[r] = n + 1;
+        num_rejected[r] = k - n;
     }
 }
 
@@ -130,8 +128,9 @@ hipError_t launch_greedy_verify(const vpa_stat* draft_stats, int32_t m_draft,
                                 int32_t n_req, int32_t k, const int32_t* draft_ids,
                                 int32_t* out_tokens, int32_t* num_sampled, int32_t* num_rejected,
                                 int32_t* target_ids, hipStream_t stream) {
-    const dim3 grid((unsigned)((n_req + kWaves - 1) / kWaves));
-    hipLaunchKernelGGL(greedy_verify_kernel, grid, dim3(kThreads), 0, stream, draft_stats, m_draft,
+    const int32_t waves = k + 1 < kVerifyMaxThreads / 64 ? k + 1 : kVerifyMaxThreads / 64;
+    hipLaunchKernelGGL(greedy_verify_kernel, dim3((unsigned)n_req), dim3(64 * waves),
+                       (size_t)(k + 1) * sizeof(int32_t), stream, draft_stats, m_draft,
                        bonus_stats, m_bonus, n_shards, n_req, k, draft_ids, out_tokens,
                        num_sampled, num_rejected, target_ids);
     return hipGetLastError();

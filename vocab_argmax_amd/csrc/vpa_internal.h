@@ -12,7 +12,9 @@ namespace vpa {
 // One launch's worth of (row, shard, slot) work items for the block-statistics
 // kernel.  Item t decodes as row i = t / (n_local*m), local shard
 // sl = (t / m) % n_local, slot j = t % m; consecutive items therefore walk a
-// row's columns in ascending order.
+// row's columns in ascending order.  Each item is scanned by a group of
+// 2^lanes_log2 lanes of one wavefront (64 / group size items per wavefront);
+// launch_block_stats picks the group size and fills lanes_log2 and n_waves.
 struct SegTask {
     const unsigned char* base;  // logits, column 0 = global column col0
     int64_t ld;                 // row stride, elements
@@ -30,6 +32,8 @@ struct SegTask {
     int32_t m;
     int32_t row_k;              // > 0: verification rows with K = row_k (rows ignored)
     int32_t row_bonus;          // with row_k > 0: 1 = bonus rows, 0 = draft rows
+    int32_t lanes_log2;         // lanes per item: 3..6 (set by launch_block_stats)
+    int32_t n_waves;            // wavefronts this task occupies (set by launch_block_stats)
 };
 
 // Launch the block-statistics kernel over the items of t0 followed by those
