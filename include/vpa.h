@@ -92,6 +92,22 @@ typedef struct {
     int32_t n_shards;    /* S >= 1, S*W >= V (a shard may hold only padding) */
 } vpa_vocab;
 
+/* Optional epilogue of the combined argmax k of a row.
+ *  d2t    draft-to-target offsets, device int64 [d2t_len], or NULL: the
+ *         mapped id is k + d2t[k] (vLLM PR #39419, note "Refactor local argmax
+ *         code": the local argmax comes first, the D2T map after it); an id
+ *         outside [0, d2t_len) maps to -1.
+ *  scale  logit scale, finite and > 0 (1.0 for none).  A positive scale
+ *         keeps the argmax (vLLM PR #34049 review: a negative one would turn
+ *         it into an argmin), so it only changes the reported maximum, which
+ *         becomes the fp32 product value*scale, rounded to nearest even with
+ *         subnormals kept; a NaN maximum is reported unchanged. */
+typedef struct {
+    const int64_t* d2t;
+    int64_t d2t_len;
+    float scale;
+} vpa_epilogue;
+
 /* Statistic slots per shard, M: the largest number of global blocks
  * [b*block, (b+1)*block) that any shard [s*W, (s+1)*W), s < S, touches
  * (PR #62604, "Purpose" item 1: global block boundaries across shard edges).
@@ -138,10 +154,14 @@ vpa_status vpa_verify_stats(const void* logits, vpa_dtype dtype, int64_t ld, vpa
  * (PR #34049, "Solution", step 3).
  *  stats    [n_shards][n_rows][m], e.g. the concatenation of every rank's
  *           vpa_block_stats output (n_shards = S, all shards present).
+ *  epi      host pointer to an epilogue, or NULL for none.
  *  ids      out, int32 [n_rows]: the global argmax of each row.
- *  val_bits out, uint32 [n_rows], or NULL: the fp32 bits of the maximum. */
+ *  val_bits out, uint32 [n_rows], or NULL: the fp32 bits of the maximum
+ *           (scaled by epi->scale).
+ *  mapped   out, int64 [n_rows]: k + d2t[k]; required iff epi->d2t is set. */
 vpa_status vpa_combine_stats(const vpa_stat* stats, int32_t n_shards, int64_t n_rows, int32_t m,
-                             int32_t* ids, uint32_t* val_bits, void* stream);
+                             const vpa_epilogue* epi, int32_t* ids, uint32_t* val_bits,
+                             int64_t* mapped, void* stream);
 
 /* Workspace bytes vpa_top_tokens needs for n_rows rows (0 if the arguments
  * are invalid or n_rows is 0). */
@@ -155,10 +175,12 @@ size_t vpa_top_tokens_workspace(vpa_vocab v, int64_t n_rows, int32_t block);
  *             c at logits[row*ld + c]); ld >= V.
  *  workspace  device memory of at least vpa_top_tokens_workspace() bytes,
  *             8-byte aligned; its contents on entry do not matter.
- *  ids, val_bits  as vpa_combine_stats (val_bits may be NULL). */
+ *  epi, ids, val_bits, mapped  as vpa_combine_stats; with epi->d2t set,
+ *             d2t_len must be at least V. */
 vpa_status vpa_top_tokens(const void* logits, vpa_dtype dtype, int64_t ld, vpa_vocab v,
                           int64_t n_rows, int32_t block, void* workspace, size_t workspace_bytes,
-                          int32_t* ids, uint32_t* val_bits, void* stream);
+                          const vpa_epilogue* epi, int32_t* ids, uint32_t* val_bits,
+                          int64_t* mapped, void* stream);
 
 /* Greedy verification from gathered statistics (PR #62604, "Purpose" item 1
  * and "Test Plan"): the target token of each position is the combined

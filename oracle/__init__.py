@@ -43,6 +43,10 @@ def _bind(lib):
     lib.vpa_ref_greedy_verify_logits.argtypes = [vp, ctypes.c_int, i64, i64, i64, i32, vp, vp,
                                                  vp, vp, vp]
     lib.vpa_ref_greedy_verify_logits.restype = None
+    lib.vpa_ref_map_ids.argtypes = [vp, i64, vp, i64, vp]
+    lib.vpa_ref_map_ids.restype = None
+    lib.vpa_ref_scale_bits.argtypes = [ctypes.c_uint32, ctypes.c_float]
+    lib.vpa_ref_scale_bits.restype = ctypes.c_uint32
     return lib
 
 
@@ -150,6 +154,21 @@ class Oracle:
         return out, ns, nr, tg
 
 
+    def map_ids(self, ids: torch.Tensor, d2t: torch.Tensor):
+        """Draft-to-target ids: ids[i] + d2t[ids[i]] (int64), -1 for ids outside d2t."""
+        ids = ids.to(torch.int32).contiguous()
+        d2t = d2t.to(torch.int64).contiguous()
+        out = torch.empty(ids.numel(), dtype=torch.int64)
+        if ids.numel():
+            self.lib.vpa_ref_map_ids(_ptr(ids), ids.numel(), _ptr(d2t), d2t.numel(), _ptr(out))
+        return out
+
+    def scale_bits(self, val_bits: torch.Tensor, scale: float):
+        """Reported maxima under a positive scale (int64 tensor of fp32 bits in, same out)."""
+        return torch.tensor([self.lib.vpa_ref_scale_bits(int(b) & 0xFFFFFFFF, scale)
+                             for b in val_bits.tolist()], dtype=torch.int64)
+
+
 def _verify_outputs(r, k):
     return (torch.empty((r, k + 1), dtype=torch.int32), torch.empty(r, dtype=torch.int32),
             torch.empty(r, dtype=torch.int32), torch.empty((r, k + 1), dtype=torch.int32))
@@ -200,3 +219,11 @@ def greedy_verify(*a, **kw):
 
 def greedy_verify_logits(*a, **kw):
     return default().greedy_verify_logits(*a, **kw)
+
+
+def map_ids(*a, **kw):
+    return default().map_ids(*a, **kw)
+
+
+def scale_bits(*a, **kw):
+    return default().scale_bits(*a, **kw)

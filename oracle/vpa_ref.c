@@ -48,6 +48,15 @@
  *    target argmax; the next position emits the target argmax (correction or
  *    bonus token); later positions hold -1; sampled = accepted + 1 and
  *    rejected = K - accepted.
+ *  - optional epilogue of the combined argmax k:
+ *    [P2] PR #39419 "[SpecDecode] Reduce TP communication for large-vocab
+ *    draft models speculative decoding", note "Refactor local argmax code":
+ *    the local argmax is taken first and the draft id then maps to a target
+ *    id as k + d2t[k];
+ *    [P1] review: a negative logit scale would turn the argmax into an
+ *    argmin, so only a positive scale is accepted; it leaves the argmax
+ *    unchanged and the reported maximum becomes fp32(value) * scale rounded
+ *    to nearest (a NaN is reported unchanged).
  */
 #include <math.h>
 #include <stdint.h>
@@ -265,4 +274,27 @@ void vpa_ref_greedy_verify_logits(const void *x, int dtype, int64_t ld, int64_t 
             for (int32_t j = 0; j <= k; ++j)
                 target_ids[r * (k + 1) + j] = tgt[j];
     }
+}
+
+/* Draft-to-target id map ([P2] "Refactor local argmax code"): out[i] =
+ * ids[i] + d2t[ids[i]]; an id outside [0, d2t_len) maps to -1. */
+void vpa_ref_map_ids(const int32_t *ids, int64_t n, const int64_t *d2t, int64_t d2t_len,
+                     int64_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = (ids[i] >= 0 && ids[i] < d2t_len) ? (int64_t)ids[i] + d2t[ids[i]] : -1;
+}
+
+/* Reported maximum under a positive logit scale: the fp32 product of the
+ * value and the scale, rounded to nearest even (the double product is exact,
+ * its conversion to float is the one rounding); a NaN is reported as is. */
+uint32_t vpa_ref_scale_bits(uint32_t bits, float scale)
+{
+    double v = ref_value(bits);
+    if (isnan(v))
+        return bits;
+    float prod = (float)(v * (double)scale);
+    uint32_t out;
+    memcpy(&out, &prod, 4);
+    return out;
 }

@@ -58,3 +58,18 @@ def verify_cases():
         out.append((int(k), [int(t) for t in tg.split()], [int(t) for t in dr.split()],
                     [int(t) for t in ot.split()], ns, nr))
     return out
+
+
+def epilogue_cases():
+    """([(value bits, scale float, expected bits)], [(d2t list, ids, expected)])"""
+    import struct
+    scales, maps = [], []
+    for line in _lines("epilogue_cases.txt"):
+        kind, a, b, c = [p.strip() for p in line.split("|")]
+        if kind == "scale":
+            scale = struct.unpack("<f", struct.pack("<I", int(b, 16)))[0]
+            scales.append((int(a, 16), scale, int(c, 16)))
+        else:
+            maps.append(([int(t) for t in a.split()], [int(t) for t in b.split()],
+                         [int(t) for t in c.split()]))
+    return scales, maps

@@ -13,7 +13,9 @@ oracle disagrees with
     that per-rank statistics concatenated in rank order equal the statistics
     of all shards at once (PR #62604, "Purpose" item 1 and "Test Plan");
   * the greedy acceptance rule, by brute force over every draft tuple of tiny
-    vocabularies.
+    vocabularies;
+  * the epilogue of the combined argmax (draft-to-target map, positive scale)
+    against hand-worked cases and torch's fp32 multiply.
 The same pins run against deliberately broken copies of the oracle
 (tests/test_oracle_mutants.py) to show that each plausible mistake is caught.
 """
@@ -213,6 +215,32 @@ def _verify_rows(n_req, k):
     return draft, bonus
 
 
+def pin_golden_epilogue(o):
+    scales, maps = golden_io.epilogue_cases()
+    for bits, scale, want in scales:
+        got = int(o.scale_bits(torch.tensor([bits]), scale)[0])
+        assert got == want, (hex(bits), scale, hex(got), hex(want))
+    for d2t, ids, want in maps:
+        got = o.map_ids(torch.tensor(ids, dtype=torch.int32), torch.tensor(d2t)).tolist()
+        assert got == want, (d2t, ids, got, want)
+
+
+def pin_scale_matches_torch(o):
+    """The scaled maximum equals torch's fp32 multiply on the CPU (IEEE, round
+    to nearest, subnormals kept) for every non-NaN value."""
+    g = torch.Generator().manual_seed(3)
+    bits = torch.cat([torch.randint(0, 2**32, (3000,), generator=g, dtype=torch.int64),
+                      torch.randint(0, 2**24, (1000,), generator=g, dtype=torch.int64),  # subnormals
+                      torch.tensor([0, 0x80000000, 0x7F800000, 0xFF800000, 0x7F7FFFFF])])
+    vals = bits.to(torch.int32).view(torch.float32)
+    keep = ~torch.isnan(vals)
+    for scale in (0.5, 0.7, 1.0, 1.4285714, 3.0, 1e-30, 7e30):
+        s32 = torch.tensor(scale, dtype=torch.float32)
+        want = (vals[keep] * s32).view(torch.int32).to(torch.int64) & 0xFFFFFFFF
+        got = o.scale_bits(bits[keep], float(s32))
+        assert torch.equal(got, want), scale
+
+
 ALL_PINS = [pin_golden_argmax, pin_golden_block_stats, pin_golden_verify, pin_exhaustive_argmax,
             pin_torch_argmax, pin_slots, pin_block_stats_bruteforce, pin_invariance,
-            pin_verify_bruteforce]
+            pin_verify_bruteforce, pin_golden_epilogue, pin_scale_matches_torch]

@@ -100,22 +100,52 @@ def test_block_stats_ld_covers_only_valid_columns(lib):
 
 def test_empty_batches_are_noops(lib):
     assert call_block_stats(lib, n_rows=0, stats=None) == vpa.VPA_OK
-    assert lib.vpa_combine_stats(None, 8, 0, 2, None, None, None) == vpa.VPA_OK
+    assert lib.vpa_combine_stats(None, 8, 0, 2, None, None, None, None, None) == vpa.VPA_OK
     assert lib.vpa_top_tokens(FAKE, vpa.VPA_BF16, 1000, V(1000, 125, 8), 0, 256, None, 0, None,
-                              None, None) == vpa.VPA_OK
+                              None, None, None, None) == vpa.VPA_OK
     assert lib.vpa_verify_stats(FAKE, vpa.VPA_F32, 1000, V(1000, 125, 8), 0, 8, 0, 3, 8192, 1024,
                                 None, None, None) == vpa.VPA_OK
     assert lib.vpa_greedy_verify(None, 1, None, 1, 8, 0, 3, None, None, None, None, None,
                                  None) == vpa.VPA_OK
 
 
+def EPI(d2t=None, n=0, scale=1.0):
+    return ctypes.pointer(vpa.Epilogue(d2t, n, scale))
+
+
 def test_combine_rejects(lib):
-    assert lib.vpa_combine_stats(FAKE, 0, 4, 2, FAKE, None, None) == vpa.VPA_ERR_INVALID
-    assert lib.vpa_combine_stats(FAKE, 2, 4, 0, FAKE, None, None) == vpa.VPA_ERR_INVALID
-    assert lib.vpa_combine_stats(None, 2, 4, 2, FAKE, None, None) == vpa.VPA_ERR_INVALID
-    assert lib.vpa_combine_stats(FAKE, 2, 4, 2, None, None, None) == vpa.VPA_ERR_INVALID
-    assert lib.vpa_combine_stats(FAKE, 2, 4, 2, FAKE, FAKE_ODD, None) == vpa.VPA_ERR_INVALID
-    assert lib.vpa_combine_stats(FAKE, 2, -1, 2, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    cs = lib.vpa_combine_stats
+    assert cs(FAKE, 0, 4, 2, None, FAKE, None, None, None) == vpa.VPA_ERR_INVALID
+    assert cs(FAKE, 2, 4, 0, None, FAKE, None, None, None) == vpa.VPA_ERR_INVALID
+    assert cs(None, 2, 4, 2, None, FAKE, None, None, None) == vpa.VPA_ERR_INVALID
+    assert cs(FAKE, 2, 4, 2, None, None, None, None, None) == vpa.VPA_ERR_INVALID
+    assert cs(FAKE, 2, 4, 2, None, FAKE, FAKE_ODD, None, None) == vpa.VPA_ERR_INVALID
+    assert cs(FAKE, 2, -1, 2, None, FAKE, None, None, None) == vpa.VPA_ERR_INVALID
+
+
+@pytest.mark.parametrize("epi,mapped", [
+    (dict(scale=0.0), None), (dict(scale=-1.0), None), (dict(scale=float("inf")), None),
+    (dict(scale=float("nan")), None),
+    (dict(d2t=0x10000, n=0), FAKE),            # empty table
+    (dict(d2t=0x10004, n=10), FAKE),           # unaligned table
+    (dict(d2t=0x10000, n=10), None),           # a table but nowhere to write the mapped ids
+    (dict(), FAKE),                             # mapped ids but no table
+    (dict(d2t=0x10000, n=10), FAKE_ODD),       # unaligned mapped ids
+])
+def test_epilogue_rejects(lib, epi, mapped):
+    assert lib.vpa_combine_stats(FAKE, 2, 4, 2, EPI(**epi), FAKE, None, mapped, None) == vpa.VPA_ERR_INVALID
+    # top_tokens also needs the table to cover the vocabulary
+    voc = V(1000, 500, 2)
+    assert lib.vpa_top_tokens(FAKE, vpa.VPA_BF16, 1000, voc, 4, 256, FAKE, 1 << 20, EPI(**epi),
+                              FAKE, None, mapped, None) == vpa.VPA_ERR_INVALID
+
+
+def test_top_tokens_d2t_must_cover_vocab(lib):
+    voc = V(1000, 500, 2)
+    call = lambda n: lib.vpa_top_tokens(FAKE, vpa.VPA_BF16, 1000, voc, 0, 256, FAKE, 1 << 20,
+                                        EPI(0x10000, n), FAKE, None, FAKE, None)
+    assert call(999) == vpa.VPA_ERR_INVALID
+    assert call(1000) == vpa.VPA_OK              # zero rows: validated, nothing enqueued
 
 
 def test_top_tokens_rejects(lib):
@@ -129,7 +159,7 @@ def test_top_tokens_rejects(lib):
     def call(**kw):
         a = {**args, **kw}
         return lib.vpa_top_tokens(FAKE, vpa.VPA_BF16, a["ld"], voc, a["n"], a["block"], a["ws"],
-                                  a["wsb"], a["ids"], None, None)
+                                  a["wsb"], None, a["ids"], None, None, None)
     assert call(wsb=need - 1) == vpa.VPA_ERR_INVALID
     assert call(ws=None) == vpa.VPA_ERR_INVALID
     assert call(ws=FAKE_ODD) == vpa.VPA_ERR_INVALID

@@ -50,6 +50,13 @@ MUTANTS = [
      "        out[j] = j < n ? draft[j] : (j == n ? (j < k ? draft[j] : target[j]) : -1);"),
     ("rejected_off_by_one",
      "    *n_rejected = k - n;", "    *n_rejected = k - n + 1;"),
+    ("map_without_draft_id",
+     "? (int64_t)ids[i] + d2t[ids[i]] : -1;", "? d2t[ids[i]] : -1;"),
+    ("nan_scaled_too",
+     "    if (isnan(v))\n        return bits;\n    float prod", "    float prod"),
+    ("scale_rounded_twice",
+     "    float prod = (float)(v * (double)scale);",
+     "    float prod = (float)((float)v * 1.0000001f * scale);"),
     ("bonus_from_last_draft_row",
      "        tgt[k] = ref_combine_row(bonus_stats, n_shards, n_req, r, m_bonus).id;",
      "        tgt[k] = tgt[k - 1];"),

@@ -128,6 +128,47 @@ def test_verify_many_drafts(k):
     _verify_both(x, vocab, w, s, n_req, k, drafts, 256, 64, f"many drafts K={k}")
 
 
+@pytest.mark.parametrize("scale", [1.0, 0.7, 1 / 0.7, 1e-40, 3e38])
+def test_epilogue_d2t_and_scale(scale):
+    """top_tokens and combine_stats with a draft-to-target table and a positive
+    scale: ids unchanged, maxima scaled in fp32 (round to nearest, subnormals
+    kept, NaN untouched, overflow to inf), mapped ids = k + d2t[k]."""
+    cases = [workloads.config2(), workloads.edge_cases()[0], workloads.edge_cases()[3]]
+    for w in cases:
+        _announce(f"epilogue {w.name} scale={scale}")
+        x_cpu, v = w.logits, w.vocab
+        g = torch.Generator().manual_seed(v)
+        d2t = torch.randint(-100, 100000, (v + 3,), generator=g, dtype=torch.int64)
+        want_ids, want_vals = oracle.argmax(x_cpu, v)
+        want_scaled = oracle.scale_bits(want_vals, scale)
+        want_mapped = oracle.map_ids(want_ids, d2t)
+        x, dd = _dev(x_cpu), _dev(d2t)
+        block = w.blocks[0]
+        ids, vals, mapped = vpa.top_tokens(x, v, w.shard_width, w.n_shards, block, d2t=dd,
+                                           scale=scale)
+        assert_same(ids, want_ids, "epilogue ids")
+        assert_same(vals.to(torch.int64) & 0xFFFFFFFF, want_scaled, "epilogue scaled values")
+        assert_same(mapped, want_mapped, "epilogue mapped ids")
+        ids2, vals2 = vpa.top_tokens(x, v, w.shard_width, w.n_shards, block, scale=scale)
+        assert_same(vals2.to(torch.int64) & 0xFFFFFFFF, want_scaled, "scale only")
+        st = vpa.block_stats(x, v, w.shard_width, w.n_shards, block)
+        ids3, vals3, mapped3 = vpa.combine_stats(st, d2t=dd, scale=scale)
+        assert_same(ids3, want_ids, "combine epilogue ids")
+        assert_same(vals3.to(torch.int64) & 0xFFFFFFFF, want_scaled, "combine scaled values")
+        assert_same(mapped3, want_mapped, "combine mapped ids")
+
+
+def test_epilogue_short_table_maps_outside_ids_to_minus_one():
+    """combine_stats accepts any table length; ids past it map to -1."""
+    w = workloads.config1()
+    x_cpu = w.logits
+    want_ids, _ = oracle.argmax(x_cpu, w.vocab)
+    d2t = torch.arange(20, dtype=torch.int64) * 3          # covers ids 0..19 only
+    st = vpa.block_stats(_dev(x_cpu), w.vocab, w.shard_width, w.n_shards, 256)
+    ids, vals, mapped = vpa.combine_stats(st, d2t=_dev(d2t))
+    assert_same(mapped, oracle.map_ids(want_ids, d2t), "short table")
+
+
 def test_row_list_out_of_range_rows_are_empty():
     case = workloads.edge_cases()[3]                      # vocab 1000, 8 shards, bf16
     x = _dev(case.logits)

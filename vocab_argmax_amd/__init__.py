@@ -50,6 +50,11 @@ class Vocab(ctypes.Structure):
                 ("n_shards", ctypes.c_int32)]
 
 
+class Epilogue(ctypes.Structure):
+    """vpa_epilogue: optional draft-to-target table and positive logit scale."""
+    _fields_ = [("d2t", ctypes.c_void_p), ("d2t_len", ctypes.c_int64), ("scale", ctypes.c_float)]
+
+
 _lib = None
 
 
@@ -63,11 +68,13 @@ def _bind(lib):
     lib.vpa_verify_stats.argtypes = [vp, ctypes.c_int, i64, Vocab, i32, i32, i64, i32, i32, i32,
                                      vp, vp, vp]
     lib.vpa_verify_stats.restype = st
-    lib.vpa_combine_stats.argtypes = [vp, i32, i64, i32, vp, vp, vp]
+    ep = ctypes.POINTER(Epilogue)
+    lib.vpa_combine_stats.argtypes = [vp, i32, i64, i32, ep, vp, vp, vp, vp]
     lib.vpa_combine_stats.restype = st
     lib.vpa_top_tokens_workspace.argtypes = [Vocab, i64, i32]
     lib.vpa_top_tokens_workspace.restype = sz
-    lib.vpa_top_tokens.argtypes = [vp, ctypes.c_int, i64, Vocab, i64, i32, vp, sz, vp, vp, vp]
+    lib.vpa_top_tokens.argtypes = [vp, ctypes.c_int, i64, Vocab, i64, i32, vp, sz, ep, vp, vp, vp,
+                                   vp]
     lib.vpa_top_tokens.restype = st
     lib.vpa_greedy_verify.argtypes = [vp, i32, vp, i32, i32, i64, i32, vp, vp, vp, vp, vp, vp]
     lib.vpa_greedy_verify.restype = st
@@ -205,14 +212,35 @@ def verify_stats(logits, vocab, shard_width, n_shards, n_req, k, block_draft=DRA
     return dst, bst
 
 
-def combine_stats(stats, stream=None):
-    """Rank-order combination of [S][N][M][2] statistics -> (ids int32[N], val_bits int32[N])."""
+def _epilogue(d2t, scale, device):
+    """(ctypes Epilogue pointer or None, d2t tensor kept alive)."""
+    if d2t is None and scale == 1.0:
+        return None, None
+    if d2t is not None:
+        if d2t.dtype != torch.int64 or not d2t.is_cuda or not d2t.is_contiguous() or d2t.dim() != 1:
+            raise ValueError("d2t must be a contiguous 1-D int64 device tensor")
+        if d2t.device != device:
+            raise ValueError(f"d2t is on {d2t.device}, expected {device}")
+    e = Epilogue(None if d2t is None else d2t.data_ptr(), 0 if d2t is None else d2t.numel(),
+                 float(scale))
+    return ctypes.pointer(e), d2t
+
+
+def combine_stats(stats, d2t=None, scale=1.0, stream=None):
+    """Rank-order combination of [S][N][M][2] statistics.
+
+    Returns (ids int32[N], val_bits int32[N]), plus mapped int64[N] = k + d2t[k]
+    when a draft-to-target table d2t is given.  A positive `scale` leaves the
+    ids and scales the reported maxima (fp32, round to nearest)."""
     _stats_tensor(stats, "stats")
     s, n, m, _ = stats.shape
     ids = torch.empty(n, dtype=torch.int32, device=stats.device)
     vals = torch.empty(n, dtype=torch.int32, device=stats.device)
-    _check(lib().vpa_combine_stats(_vp(stats), s, n, m, _vp(ids), _vp(vals), _stream(stream)))
-    return ids, vals
+    mapped = torch.empty(n, dtype=torch.int64, device=stats.device) if d2t is not None else None
+    epi, _keep = _epilogue(d2t, scale, stats.device)
+    _check(lib().vpa_combine_stats(_vp(stats), s, n, m, epi, _vp(ids), _vp(vals), _vp(mapped),
+                                   _stream(stream)))
+    return (ids, vals) if d2t is None else (ids, vals, mapped)
 
 
 def top_tokens_workspace(vocab, shard_width, n_shards, n_rows, block=DRAFT_BLOCK) -> int:
@@ -220,11 +248,13 @@ def top_tokens_workspace(vocab, shard_width, n_shards, n_rows, block=DRAFT_BLOCK
 
 
 def top_tokens(logits, vocab, shard_width, n_shards, block=DRAFT_BLOCK, workspace=None,
-               ids=None, val_bits=None, stream=None):
-    """Fused get_top_tokens over all shards of each row -> (ids int32[N], val_bits int32[N]).
+               ids=None, val_bits=None, d2t=None, scale=1.0, mapped=None, stream=None):
+    """Fused get_top_tokens over all shards of each row -> (ids int32[N], val_bits int32[N]),
+    plus mapped int64[N] = k + d2t[k] when a draft-to-target table is given.
 
     logits [N, ld] holds the S shards side by side (ld >= vocab).  workspace:
     optional uint8 device tensor of at least top_tokens_workspace() bytes.
+    scale: positive logit scale; it leaves the ids and scales the maxima.
     """
     ld = _logits_ld(logits)
     n = logits.shape[0]
@@ -235,11 +265,15 @@ def top_tokens(logits, vocab, shard_width, n_shards, block=DRAFT_BLOCK, workspac
         ids = torch.empty(n, dtype=torch.int32, device=logits.device)
     if val_bits is None:
         val_bits = torch.empty(n, dtype=torch.int32, device=logits.device)
+    if d2t is not None and mapped is None:
+        mapped = torch.empty(n, dtype=torch.int64, device=logits.device)
+    epi, _keep = _epilogue(d2t, scale, logits.device)
     _check(lib().vpa_top_tokens(_vp(logits), _dtype_code(logits), ld,
                                 Vocab(vocab, shard_width, n_shards), n, block, _vp(workspace),
-                                workspace.numel() * workspace.element_size(), _vp(ids),
-                                _vp(val_bits), _stream(stream)))
-    return ids, val_bits
+                                workspace.numel() * workspace.element_size(), epi, _vp(ids),
+                                _vp(val_bits), _vp(mapped if d2t is not None else None),
+                                _stream(stream)))
+    return (ids, val_bits) if d2t is None else (ids, val_bits, mapped)
 
 
 def greedy_verify(draft_stats, bonus_stats, draft_ids, with_targets=True, out=None,

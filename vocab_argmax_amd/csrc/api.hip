@@ -1,6 +1,7 @@
 // api.hip -- the C ABI of include/vpa.h: host-side validation, sizing and
 // launches.  No HIP call happens before every argument has been checked, so
 // invalid calls enqueue nothing and can be exercised without a GPU.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -117,6 +118,37 @@ vpa_status check_logits_ptr(const void* logits, vpa_dtype dt) {
     return ok();
 }
 
+// The epilogue, resolved: no map and scale 1 when epi is NULL.
+struct Epi {
+    const int64_t* d2t = nullptr;
+    int64_t d2t_len = 0;
+    float scale = 1.0f;
+};
+
+vpa_status check_epilogue(const vpa_epilogue* epi, int64_t min_len, int64_t* mapped, Epi& e) {
+    e = Epi{};
+    if (epi) {
+        if (!(epi->scale > 0.0f) || !isfinite(epi->scale))
+            return fail(VPA_ERR_INVALID, "epilogue scale %g is not finite and positive",
+                        (double)epi->scale);
+        e.scale = epi->scale;
+        if (epi->d2t) {
+            if (epi->d2t_len < min_len || epi->d2t_len < 1)
+                return fail(VPA_ERR_INVALID, "d2t_len %lld < %lld", (long long)epi->d2t_len,
+                            (long long)(min_len > 1 ? min_len : 1));
+            if (!aligned(epi->d2t, 8))
+                return fail(VPA_ERR_INVALID, "d2t not 8-byte aligned");
+            e.d2t = epi->d2t;
+            e.d2t_len = epi->d2t_len;
+        }
+    }
+    if ((e.d2t != nullptr) != (mapped != nullptr))
+        return fail(VPA_ERR_INVALID, "mapped ids are required exactly when a d2t table is given");
+    if (mapped && !aligned(mapped, 8))
+        return fail(VPA_ERR_INVALID, "mapped not 8-byte aligned");
+    return ok();
+}
+
 vpa_status set_items(vpa::SegTask& t, int64_t n_rows, const char* what) {
     const int64_t items = n_rows * t.n_local * (int64_t)t.m;
     if (n_rows > INT32_MAX || items > INT32_MAX)
@@ -208,20 +240,25 @@ vpa_status vpa_verify_stats(const void* logits, vpa_dtype dtype, int64_t ld, vpa
 }
 
 vpa_status vpa_combine_stats(const vpa_stat* stats, int32_t n_shards, int64_t n_rows, int32_t m,
-                             int32_t* ids, uint32_t* val_bits, void* stream) {
+                             const vpa_epilogue* epi, int32_t* ids, uint32_t* val_bits,
+                             int64_t* mapped, void* stream) {
     if (n_shards < 1 || m < 1 || (int64_t)n_shards * m > INT32_MAX)
         return fail(VPA_ERR_INVALID, "n_shards %d / m %d invalid", (int)n_shards, (int)m);
     if (n_rows < 0 || n_rows > INT32_MAX)
         return fail(VPA_ERR_INVALID, "n_rows %lld out of range", (long long)n_rows);
+    Epi e;
+    vpa_status st = check_epilogue(epi, 1, mapped, e);
+    if (st != VPA_OK)
+        return st;
     if (n_rows == 0)
         return ok();
     if (!stats || !aligned(stats, 8))
         return fail(VPA_ERR_INVALID, "stats is NULL or not 8-byte aligned");
     if (!ids || !aligned(ids, 4) || (val_bits && !aligned(val_bits, 4)))
         return fail(VPA_ERR_INVALID, "ids is NULL, or ids/val_bits not 4-byte aligned");
-    hipError_t e = vpa::launch_combine(stats, n_shards, (int32_t)n_rows, m, ids, val_bits,
-                                       (hipStream_t)stream);
-    return e == hipSuccess ? ok() : hip_fail(e, "vpa_combine_stats launch");
+    hipError_t he = vpa::launch_combine(stats, n_shards, (int32_t)n_rows, m, e.d2t, e.d2t_len,
+                                        e.scale, ids, val_bits, mapped, (hipStream_t)stream);
+    return he == hipSuccess ? ok() : hip_fail(he, "vpa_combine_stats launch");
 }
 
 size_t vpa_top_tokens_workspace(vpa_vocab v, int64_t n_rows, int32_t block) {
@@ -236,10 +273,14 @@ size_t vpa_top_tokens_workspace(vpa_vocab v, int64_t n_rows, int32_t block) {
 
 vpa_status vpa_top_tokens(const void* logits, vpa_dtype dtype, int64_t ld, vpa_vocab v,
                           int64_t n_rows, int32_t block, void* workspace, size_t workspace_bytes,
-                          int32_t* ids, uint32_t* val_bits, void* stream) {
+                          const vpa_epilogue* epi, int32_t* ids, uint32_t* val_bits,
+                          int64_t* mapped, void* stream) {
     vpa::SegTask t;
     vpa_status st = check_logits_task(logits, dtype, ld, v, 0, v.n_shards, block, t);
     if (st != VPA_OK)
+        return st;
+    Epi ep;
+    if ((st = check_epilogue(epi, v.vocab, mapped, ep)) != VPA_OK)
         return st;
     if (n_rows < 0)
         return fail(VPA_ERR_INVALID, "n_rows %lld < 0", (long long)n_rows);
@@ -260,8 +301,8 @@ vpa_status vpa_top_tokens(const void* logits, vpa_dtype dtype, int64_t ld, vpa_v
     hipError_t e = vpa::launch_block_stats(esize_of(dtype), t, none, (hipStream_t)stream);
     if (e != hipSuccess)
         return hip_fail(e, "vpa_top_tokens statistics launch");
-    e = vpa::launch_combine(t.stats, v.n_shards, (int32_t)n_rows, t.m, ids, val_bits,
-                            (hipStream_t)stream);
+    e = vpa::launch_combine(t.stats, v.n_shards, (int32_t)n_rows, t.m, ep.d2t, ep.d2t_len,
+                            ep.scale, ids, val_bits, mapped, (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "vpa_top_tokens combine launch");
 }
 

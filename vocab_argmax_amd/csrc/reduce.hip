@@ -48,10 +48,22 @@ __device__ __forceinline__ void row_best(const vpa_stat* __restrict__ stats, int
     bits = bb;
 }
 
-__global__ __launch_bounds__(kThreads) void combine_kernel(const vpa_stat* __restrict__ stats,
-                                                           int32_t n_shards, int32_t n_rows,
-                                                           int32_t m, int32_t* __restrict__ ids,
-                                                           uint32_t* __restrict__ val_bits) {
+// Reported maximum under a positive logit scale: the IEEE fp32 product,
+// rounded to nearest even (the kernel runs with fp32 denormals preserved);
+// a NaN is passed through untouched.
+__device__ __forceinline__ uint32_t scaled_bits(uint32_t bits, float scale) {
+    if ((bits & 0x7FFFFFFFu) > 0x7F800000u)
+        return bits;
+    return __float_as_uint(__fmul_rn(__uint_as_float(bits), scale));
+}
+
+// One wavefront per row; the epilogue (vLLM PR #39419, "Refactor local
+// argmax code": map the argmax k to k + d2t[k]; a positive scale changes only
+// the reported maximum) runs on lane 0 after the reduction.
+__global__ __launch_bounds__(kThreads) void combine_kernel(
+    const vpa_stat* __restrict__ stats, int32_t n_shards, int32_t n_rows, int32_t m,
+    const int64_t* __restrict__ d2t, int64_t d2t_len, float scale, int32_t* __restrict__ ids,
+    uint32_t* __restrict__ val_bits, int64_t* __restrict__ mapped) {
     const int lane = threadIdx.x & 63;
     const int32_t wave = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
     const int32_t row = (int32_t)blockIdx.x * kWaves + wave;
@@ -63,7 +75,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const vpa_stat* __res
     if (lane == 0) {
         ids[row] = id;
         if (val_bits)
-            val_bits[row] = bits;
+            val_bits[row] = scale == 1.0f ? bits : scaled_bits(bits, scale);
+        if (mapped)
+            mapped[row] = (id >= 0 && id < d2t_len) ? (int64_t)id + d2t[id] : -1;
     }
 }
 
@@ -116,10 +130,11 @@ __global__ __launch_bounds__(kVerifyMaxThreads) void greedy_verify_kernel(
 }  // namespace
 
 hipError_t launch_combine(const vpa_stat* stats, int32_t n_shards, int32_t n_rows, int32_t m,
-                          int32_t* ids, uint32_t* val_bits, hipStream_t stream) {
+                          const int64_t* d2t, int64_t d2t_len, float scale, int32_t* ids,
+                          uint32_t* val_bits, int64_t* mapped, hipStream_t stream) {
     const dim3 grid((unsigned)((n_rows + kWaves - 1) / kWaves));
     hipLaunchKernelGGL(combine_kernel, grid, dim3(kThreads), 0, stream, stats, n_shards, n_rows, m,
-                       ids, val_bits);
+                       d2t, d2t_len, scale, ids, val_bits, mapped);
     return hipGetLastError();
 }
 

@@ -40,8 +40,11 @@ struct SegTask {
 // of t1 (t1.n_items may be 0).  Both tasks share dtype `esize` (2 or 4).
 hipError_t launch_block_stats(int esize, const SegTask& t0, const SegTask& t1, hipStream_t stream);
 
+// Combine with the epilogue already validated: d2t may be null (then mapped
+// is null too); scale is finite and positive.
 hipError_t launch_combine(const vpa_stat* stats, int32_t n_shards, int32_t n_rows, int32_t m,
-                          int32_t* ids, uint32_t* val_bits, hipStream_t stream);
+                          const int64_t* d2t, int64_t d2t_len, float scale, int32_t* ids,
+                          uint32_t* val_bits, int64_t* mapped, hipStream_t stream);
 
 hipError_t launch_greedy_verify(const vpa_stat* draft_stats, int32_t m_draft,
                                 const vpa_stat* bonus_stats, int32_t m_bonus, int32_t n_shards,
