@@ -43,6 +43,12 @@ def _bind(lib):
     lib.vpa_ref_greedy_verify_logits.argtypes = [vp, ctypes.c_int, i64, i64, i64, i32, vp, vp,
                                                  vp, vp, vp]
     lib.vpa_ref_greedy_verify_logits.restype = None
+    lib.vpa_ref_greedy_verify_ragged.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, vp,
+                                                 vp, vp]
+    lib.vpa_ref_greedy_verify_ragged.restype = None
+    lib.vpa_ref_greedy_verify_ragged_stats.argtypes = [vp, i32, vp, i32, i32, i64, vp, vp, vp, vp,
+                                                       vp, vp]
+    lib.vpa_ref_greedy_verify_ragged_stats.restype = None
     lib.vpa_ref_map_ids.argtypes = [vp, i64, vp, i64, vp]
     lib.vpa_ref_map_ids.restype = None
     lib.vpa_ref_scale_bits.argtypes = [ctypes.c_uint32, ctypes.c_float]
@@ -154,6 +160,48 @@ class Oracle:
         return out, ns, nr, tg
 
 
+    def greedy_verify_ragged(self, x: torch.Tensor, vocab: int, cu: torch.Tensor,
+                             draft_ids: torch.Tensor):
+        """Ragged greedy verification from full logits.  cu int32 [R+1] cumulative
+        draft counts; request r owns rows cu[r]+r..cu[r]+r+K_r.  Returns
+        (out_tokens [cu[R]+R], num_sampled [R], num_rejected [R], target_ids [cu[R]+R])."""
+        ld = _check_logits(x)
+        cu = cu.to(torch.int32).contiguous()
+        draft_ids = draft_ids.to(torch.int32).contiguous()
+        r = cu.numel() - 1
+        total = int(cu[-1]) if r > 0 else 0
+        if x.shape[0] < total + r:
+            raise ValueError("logits have fewer rows than drafts + requests")
+        out = torch.empty(total + r, dtype=torch.int32)
+        ns = torch.empty(r, dtype=torch.int32)
+        nr = torch.empty(r, dtype=torch.int32)
+        tg = torch.empty(total + r, dtype=torch.int32)
+        if r:
+            self.lib.vpa_ref_greedy_verify_ragged(_ptr(x), _dtype_code(x), ld, vocab, r, _ptr(cu),
+                                                  _ptr(draft_ids), _ptr(out), _ptr(ns), _ptr(nr),
+                                                  _ptr(tg))
+        return out, ns, nr, tg
+
+    def greedy_verify_ragged_stats(self, draft_stats: torch.Tensor, bonus_stats: torch.Tensor,
+                                   cu: torch.Tensor, draft_ids: torch.Tensor):
+        """Ragged greedy verification from statistics [S][cu[R]][Md][2], [S][R][Mb][2]."""
+        draft_stats = draft_stats.contiguous()
+        bonus_stats = bonus_stats.contiguous()
+        cu = cu.to(torch.int32).contiguous()
+        draft_ids = draft_ids.to(torch.int32).contiguous()
+        r = cu.numel() - 1
+        total = int(cu[-1]) if r > 0 else 0
+        s, md, mb = draft_stats.shape[0], draft_stats.shape[2], bonus_stats.shape[2]
+        out = torch.empty(total + r, dtype=torch.int32)
+        ns = torch.empty(r, dtype=torch.int32)
+        nr = torch.empty(r, dtype=torch.int32)
+        tg = torch.empty(total + r, dtype=torch.int32)
+        if r:
+            self.lib.vpa_ref_greedy_verify_ragged_stats(_ptr(draft_stats), md, _ptr(bonus_stats),
+                                                        mb, s, r, _ptr(cu), _ptr(draft_ids),
+                                                        _ptr(out), _ptr(ns), _ptr(nr), _ptr(tg))
+        return out, ns, nr, tg
+
     def map_ids(self, ids: torch.Tensor, d2t: torch.Tensor):
         """Draft-to-target ids: ids[i] + d2t[ids[i]] (int64), -1 for ids outside d2t."""
         ids = ids.to(torch.int32).contiguous()
@@ -172,6 +220,18 @@ class Oracle:
 def _verify_outputs(r, k):
     return (torch.empty((r, k + 1), dtype=torch.int32), torch.empty(r, dtype=torch.int32),
             torch.empty(r, dtype=torch.int32), torch.empty((r, k + 1), dtype=torch.int32))
+
+
+def ragged_rows(cu: torch.Tensor):
+    """Row lists of a ragged verification batch: draft rows cu[r]+r+j (j < K_r)
+    back to back, and bonus rows cu[r+1]+r."""
+    cu = cu.to(torch.int64)
+    r = cu.numel() - 1
+    counts = cu[1:] - cu[:-1]
+    req = torch.repeat_interleave(torch.arange(r), counts)
+    draft = (torch.arange(int(cu[-1])) + req).to(torch.int32)
+    bonus = (cu[1:] + torch.arange(r)).to(torch.int32)
+    return draft, bonus
 
 
 def verify_rows(n_req: int, k: int):
@@ -227,3 +287,11 @@ def map_ids(*a, **kw):
 
 def scale_bits(*a, **kw):
     return default().scale_bits(*a, **kw)
+
+
+def greedy_verify_ragged(*a, **kw):
+    return default().greedy_verify_ragged(*a, **kw)
+
+
+def greedy_verify_ragged_stats(*a, **kw):
+    return default().greedy_verify_ragged_stats(*a, **kw)

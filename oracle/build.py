@@ -13,12 +13,13 @@ LIB = os.path.join(HERE, "libvpa_ref.so")
 def build(verbose: bool = False, src: str = SRC, lib: str = LIB, strict: bool = True) -> str:
     # -fno-fast-math and no -ffinite-math: the oracle relies on IEEE NaN
     # comparisons; -O2 keeps the scalar loops fast enough for the CPU baseline.
+    tmp = f"{lib}.{os.getpid()}.tmp"   # concurrent builders never share a temporary
     cmd = ["gcc", "-O2", "-std=gnu99", "-Wall", "-Wextra", "-fno-fast-math",
-           "-shared", "-fPIC", src, "-o", lib + ".tmp"] + (["-Werror"] if strict else [])
+           "-shared", "-fPIC", src, "-o", tmp] + (["-Werror"] if strict else [])
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    os.replace(lib + ".tmp", lib)
+    os.replace(tmp, lib)
     return lib
 
 

@@ -48,6 +48,11 @@
  *    target argmax; the next position emits the target argmax (correction or
  *    bonus token); later positions hold -1; sampled = accepted + 1 and
  *    rejected = K - accepted.
+ *  - ragged verification: request r carries K_r >= 0 drafts given by
+ *    cumulative offsets cu[0..R] (cu[0] = 0, K_r = cu[r+1] - cu[r]); its
+ *    logits rows are cu[r]+r .. cu[r]+r+K_r (drafts, then the bonus
+ *    position) and its K_r+1 outputs sit at the same offsets; the greedy
+ *    rule is the uniform one with K = K_r (K_r = 0 emits the bonus token).
  *  - optional epilogue of the combined argmax k:
  *    [P2] PR #39419 "[SpecDecode] Reduce TP communication for large-vocab
  *    draft models speculative decoding", note "Refactor local argmax code":
@@ -297,4 +302,53 @@ uint32_t vpa_ref_scale_bits(uint32_t bits, float scale)
     uint32_t out;
     memcpy(&out, &prod, 4);
     return out;
+}
+
+/* Ragged greedy verification from full logits: request r owns rows
+ * cu[r]+r .. cu[r]+r+K_r (K_r = cu[r+1]-cu[r] drafts, then the bonus row);
+ * draft_ids holds the cu[R] drafts back to back; out_tokens and target_ids
+ * hold K_r+1 entries per request at offset cu[r]+r. */
+void vpa_ref_greedy_verify_ragged(const void *x, int dtype, int64_t ld, int64_t vocab, int64_t n_req,
+                                  const int32_t *cu, const int32_t *draft_ids, int32_t *out_tokens,
+                                  int32_t *num_sampled, int32_t *num_rejected, int32_t *target_ids)
+{
+    for (int64_t r = 0; r < n_req; ++r) {
+        int32_t k = cu[r + 1] - cu[r];
+        int64_t base = (int64_t)cu[r] + r;
+        int32_t tgt[k + 1];
+        uint32_t vb;
+        for (int32_t j = 0; j <= k; ++j) {
+            const char *row = (const char *)x + (dtype == REF_BF16 ? 2 : 4) * (base + j) * ld;
+            vpa_ref_argmax(row, dtype, ld, 1, vocab, &tgt[j], &vb);
+        }
+        ref_accept(draft_ids + cu[r], tgt, k, out_tokens + base, num_sampled + r, num_rejected + r);
+        if (target_ids)
+            for (int32_t j = 0; j <= k; ++j)
+                target_ids[base + j] = tgt[j];
+    }
+}
+
+/* Ragged greedy verification from gathered statistics: draft_stats
+ * [S][cu[R]][m_draft] (row cu[r]+j is draft position j of request r),
+ * bonus_stats [S][R][m_bonus]; outputs as vpa_ref_greedy_verify_ragged. */
+void vpa_ref_greedy_verify_ragged_stats(const ref_stat *draft_stats, int32_t m_draft,
+                                        const ref_stat *bonus_stats, int32_t m_bonus,
+                                        int32_t n_shards, int64_t n_req, const int32_t *cu,
+                                        const int32_t *draft_ids, int32_t *out_tokens,
+                                        int32_t *num_sampled, int32_t *num_rejected,
+                                        int32_t *target_ids)
+{
+    int64_t total = cu[n_req];
+    for (int64_t r = 0; r < n_req; ++r) {
+        int32_t k = cu[r + 1] - cu[r];
+        int64_t base = (int64_t)cu[r] + r;
+        int32_t tgt[k + 1];
+        for (int32_t j = 0; j < k; ++j)
+            tgt[j] = ref_combine_row(draft_stats, n_shards, total, (int64_t)cu[r] + j, m_draft).id;
+        tgt[k] = ref_combine_row(bonus_stats, n_shards, n_req, r, m_bonus).id;
+        ref_accept(draft_ids + cu[r], tgt, k, out_tokens + base, num_sampled + r, num_rejected + r);
+        if (target_ids)
+            for (int32_t j = 0; j <= k; ++j)
+                target_ids[base + j] = tgt[j];
+    }
 }

@@ -73,3 +73,12 @@ def epilogue_cases():
             maps.append(([int(t) for t in a.split()], [int(t) for t in b.split()],
                          [int(t) for t in c.split()]))
     return scales, maps
+
+
+def ragged_verify_cases():
+    """[(cu, targets, drafts, out_tokens, sampled, rejected)] as int lists."""
+    out = []
+    for line in _lines("ragged_verify_cases.txt"):
+        fields = [[int(t) for t in p.split()] for p in line.split("|")]
+        out.append(tuple(fields))
+    return out

@@ -241,6 +241,54 @@ def pin_scale_matches_torch(o):
         assert torch.equal(got, want), scale
 
 
+def _ragged_logits(targets, vocab):
+    """Rows whose only maximum sits at the given target ids."""
+    x = torch.zeros((len(targets), vocab), dtype=torch.float32)
+    for i, t in enumerate(targets):
+        x[i, t] = 1.0
+    return x
+
+
+def pin_ragged_verify(o):
+    """Ragged verification: hand-worked cases; every request equals the
+    brute-force greedy rule with its own K; statistics and logits agree."""
+    import oracle as _oracle
+    for cu, targets, drafts, out, ns, nr in golden_io.ragged_verify_cases():
+        x = _ragged_logits(targets, 16)
+        cu_t = torch.tensor(cu, dtype=torch.int32)
+        d = torch.tensor(drafts, dtype=torch.int32)
+        got = o.greedy_verify_ragged(x, 16, cu_t, d)
+        assert got[0].tolist() == out and got[1].tolist() == ns and got[2].tolist() == nr, \
+            (cu, got)
+        assert got[3].tolist() == targets
+    rng = random.Random(5)
+    for trial in range(200):
+        vocab = rng.randint(1, 4)
+        n_req = rng.randint(1, 6)
+        ks = [rng.randint(0, 4) for _ in range(n_req)]
+        cu = [0]
+        for k in ks:
+            cu.append(cu[-1] + k)
+        targets = [rng.randrange(vocab) for _ in range(cu[-1] + n_req)]
+        drafts = [rng.randint(-1, vocab - 1) for _ in range(cu[-1])]
+        x = _ragged_logits(targets, vocab)
+        cu_t = torch.tensor(cu, dtype=torch.int32)
+        d = torch.tensor(drafts, dtype=torch.int32)
+        out, ns, nr, tg = o.greedy_verify_ragged(x, vocab, cu_t, d)
+        draft_rows, bonus_rows = _oracle.ragged_rows(cu_t)
+        dst = o.block_stats(x, vocab, vocab, 1, 1, rows=draft_rows)
+        bst = o.block_stats(x, vocab, vocab, 1, 1, rows=bonus_rows)
+        got2 = o.greedy_verify_ragged_stats(dst, bst, cu_t, d)
+        for a, b in zip((out, ns, nr, tg), got2):
+            assert torch.equal(a, b), (cu, drafts)
+        for r, k in enumerate(ks):
+            base = cu[r] + r
+            want = bf.bf_verify(targets[base:base + k + 1], drafts[cu[r]:cu[r] + k])
+            got = (out[base:base + k + 1].tolist(), int(ns[r]), int(nr[r]))
+            assert got == want, (cu, r, got, want)
+
+
 ALL_PINS = [pin_golden_argmax, pin_golden_block_stats, pin_golden_verify, pin_exhaustive_argmax,
             pin_torch_argmax, pin_slots, pin_block_stats_bruteforce, pin_invariance,
-            pin_verify_bruteforce, pin_golden_epilogue, pin_scale_matches_torch]
+            pin_verify_bruteforce, pin_golden_epilogue, pin_scale_matches_torch,
+            pin_ragged_verify]

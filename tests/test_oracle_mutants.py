@@ -50,6 +50,12 @@ MUTANTS = [
      "        out[j] = j < n ? draft[j] : (j == n ? (j < k ? draft[j] : target[j]) : -1);"),
     ("rejected_off_by_one",
      "    *n_rejected = k - n;", "    *n_rejected = k - n + 1;"),
+    ("ragged_rows_without_request_offset",
+     "        int64_t base = (int64_t)cu[r] + r;\n        int32_t tgt[k + 1];\n        uint32_t vb;",
+     "        int64_t base = (int64_t)cu[r];\n        int32_t tgt[k + 1];\n        uint32_t vb;"),
+    ("ragged_stats_bonus_from_draft_rows",
+     "        tgt[k] = ref_combine_row(bonus_stats, n_shards, n_req, r, m_bonus).id;\n        ref_accept(draft_ids + cu[r]",
+     "        tgt[k] = k ? tgt[k - 1] : 0;\n        ref_accept(draft_ids + cu[r]"),
     ("map_without_draft_id",
      "? (int64_t)ids[i] + d2t[ids[i]] : -1;", "? d2t[ids[i]] : -1;"),
     ("nan_scaled_too",
@@ -58,8 +64,8 @@ MUTANTS = [
      "    float prod = (float)(v * (double)scale);",
      "    float prod = (float)((float)v * 1.0000001f * scale);"),
     ("bonus_from_last_draft_row",
-     "        tgt[k] = ref_combine_row(bonus_stats, n_shards, n_req, r, m_bonus).id;",
-     "        tgt[k] = tgt[k - 1];"),
+     "r * k + j, m_draft).id;\n        tgt[k] = ref_combine_row(bonus_stats, n_shards, n_req, r, m_bonus).id;",
+     "r * k + j, m_draft).id;\n        tgt[k] = tgt[k - 1];"),
 ]
 
 
