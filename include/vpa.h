@@ -150,6 +150,32 @@ vpa_status vpa_verify_stats(const void* logits, vpa_dtype dtype, int64_t ld, vpa
                             int32_t block_draft, int32_t block_bonus, vpa_stat* draft_stats,
                             vpa_stat* bonus_stats, void* stream);
 
+/* Statistics of a verification batch given by two row lists, in one launch:
+ * draft rows with block_draft, bonus rows with block_bonus (PR #62604,
+ * "Purpose" item 1).  Other arguments as vpa_block_stats; rows outside
+ * [0, logits_rows) give empty statistics.
+ *  draft_stats  out, [n_local_shards][n_draft_rows][M_draft]
+ *  bonus_stats  out, [n_local_shards][n_bonus_rows][M_bonus] */
+vpa_status vpa_verify_stats_rows(const void* logits, vpa_dtype dtype, int64_t ld, vpa_vocab v,
+                                 int32_t first_shard, int32_t n_local_shards,
+                                 const int32_t* draft_rows, int64_t n_draft_rows,
+                                 const int32_t* bonus_rows, int64_t n_bonus_rows,
+                                 int64_t logits_rows, int32_t block_draft, int32_t block_bonus,
+                                 vpa_stat* draft_stats, vpa_stat* bonus_stats, void* stream);
+
+/* Row lists of a ragged verification batch (per-request draft counts).
+ *  cu           device int32 [n_req+1], cumulative draft counts: cu[0] = 0,
+ *               request r carries K_r = cu[r+1] - cu[r] drafts, cu[n_req] =
+ *               total_drafts.  Request r owns logits rows cu[r]+r ..
+ *               cu[r]+r+K_r: its K_r draft positions, then its bonus position.
+ *  draft_rows   out, int32 [total_drafts]: draft position j of request r at
+ *               index cu[r]+j holds row cu[r]+r+j.
+ *  bonus_rows   out, int32 [n_req]: row cu[r+1]+r.
+ * Offsets that break the rules above give unspecified rows (any row outside
+ * the logits then yields empty statistics) but no access out of bounds. */
+vpa_status vpa_ragged_rows(const int32_t* cu, int64_t n_req, int64_t total_drafts,
+                           int32_t* draft_rows, int32_t* bonus_rows, void* stream);
+
 /* Rank-order combination of gathered statistics into the global argmax
  * (PR #34049, "Solution", step 3).
  *  stats    [n_shards][n_rows][m], e.g. the concatenation of every rank's
@@ -202,6 +228,27 @@ vpa_status vpa_greedy_verify(const vpa_stat* draft_stats, int32_t m_draft,
                              int64_t n_req, int32_t k, const int32_t* draft_ids,
                              int32_t* out_tokens, int32_t* num_sampled, int32_t* num_rejected,
                              int32_t* target_ids, void* stream);
+
+/* Ragged greedy verification from gathered statistics: as
+ * vpa_greedy_verify with a draft count per request.
+ *  cu           device int32 [n_req+1] as for vpa_ragged_rows.
+ *  draft_stats  [n_shards][total_drafts][m_draft] (row cu[r]+j = draft j of r),
+ *  bonus_stats  [n_shards][n_req][m_bonus].
+ *  draft_ids    int32 [total_drafts], request r's drafts at cu[r]...
+ *  out_tokens   out, int32 [total_drafts + n_req]: request r's K_r+1 entries
+ *               at cu[r]+r (accepted drafts, then the correction or bonus
+ *               token, then -1); a request with K_r = 0 emits its bonus token.
+ *  num_sampled, num_rejected  out, int32 [n_req]: accepted+1 and K_r-accepted;
+ *               both -1 for a request whose offsets are malformed (K_r < 0,
+ *               K_r > VPA_MAX_DRAFTS, or outside [0, total_drafts]), which then
+ *               writes no tokens.
+ *  target_ids   out, int32 [total_drafts + n_req] or NULL. */
+vpa_status vpa_greedy_verify_ragged(const vpa_stat* draft_stats, int32_t m_draft,
+                                    const vpa_stat* bonus_stats, int32_t m_bonus,
+                                    int32_t n_shards, int64_t n_req, const int32_t* cu,
+                                    int64_t total_drafts, const int32_t* draft_ids,
+                                    int32_t* out_tokens, int32_t* num_sampled,
+                                    int32_t* num_rejected, int32_t* target_ids, void* stream);
 
 /* Message describing the last non-OK status returned on the calling thread
  * ("" if none).  The pointer stays valid until the next call on that thread. */

@@ -192,3 +192,32 @@ def test_verify_rejects(lib):
 def test_last_error_is_per_call_message(lib):
     call_block_stats(lib, block=0)
     assert "block" in vpa.last_error()
+
+
+def test_ragged_rejects(lib):
+    voc = V(200064, 50016, 4)
+    vsr = lib.vpa_verify_stats_rows
+    assert vsr(FAKE, vpa.VPA_BF16, 200064, voc, 0, 4, FAKE, -1, FAKE, 2, 8, 8192, 1024, FAKE,
+               FAKE, None) == vpa.VPA_ERR_INVALID
+    assert vsr(FAKE, vpa.VPA_BF16, 200064, voc, 0, 4, None, 6, FAKE, 2, 8, 8192, 1024, FAKE,
+               FAKE, None) == vpa.VPA_ERR_INVALID
+    assert vsr(FAKE, vpa.VPA_BF16, 200064, voc, 0, 4, FAKE, 6, FAKE_ODD, 2, 8, 8192, 1024, FAKE,
+               FAKE, None) == vpa.VPA_ERR_INVALID
+    assert vsr(FAKE, vpa.VPA_BF16, 200064, voc, 0, 4, FAKE, 6, FAKE, 2, 8, 0, 1024, FAKE,
+               FAKE, None) == vpa.VPA_ERR_INVALID
+    assert vsr(None, vpa.VPA_BF16, 200064, voc, 0, 4, None, 0, None, 0, 0, 8192, 1024, None,
+               None, None) == vpa.VPA_OK                       # nothing to do
+    rr = lib.vpa_ragged_rows
+    assert rr(FAKE, -1, 0, FAKE, FAKE, None) == vpa.VPA_ERR_INVALID
+    assert rr(FAKE, 3, -1, FAKE, FAKE, None) == vpa.VPA_ERR_INVALID
+    assert rr(None, 3, 4, FAKE, FAKE, None) == vpa.VPA_ERR_INVALID
+    assert rr(FAKE, 3, 4, None, FAKE, None) == vpa.VPA_ERR_INVALID
+    assert rr(FAKE_ODD, 3, 4, FAKE, FAKE, None) == vpa.VPA_ERR_INVALID
+    assert rr(None, 0, 0, None, None, None) == vpa.VPA_OK
+    gr = lib.vpa_greedy_verify_ragged
+    assert gr(FAKE, 0, FAKE, 50, 4, 3, FAKE, 6, FAKE, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert gr(FAKE, 7, FAKE, 50, 4, 3, None, 6, FAKE, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert gr(FAKE, 7, FAKE, 50, 4, 3, FAKE, 6, None, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert gr(FAKE, 7, FAKE, 50, 4, 3, FAKE, 6, FAKE, FAKE, FAKE, FAKE, FAKE_ODD, None) == vpa.VPA_ERR_INVALID
+    assert gr(FAKE, 7, FAKE, 50, 4, -2, FAKE, 6, FAKE, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert gr(None, 7, None, 50, 4, 0, None, 0, None, None, None, None, None, None) == vpa.VPA_OK

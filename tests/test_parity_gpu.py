@@ -169,6 +169,74 @@ def test_epilogue_short_table_maps_outside_ids_to_minus_one():
     assert_same(mapped, oracle.map_ids(want_ids, d2t), "short table")
 
 
+def _ragged_case(seed, vocab, s, n_req, kmax, dtype=torch.bfloat16, p_copy=0.7):
+    g = torch.Generator().manual_seed(seed)
+    ks = torch.randint(0, kmax + 1, (n_req,), generator=g)
+    cu = torch.zeros(n_req + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(ks, 0).to(torch.int32)
+    total = int(cu[-1])
+    w = -(-vocab // s)
+    x = (torch.randn((total + n_req, s * w), generator=g) * 3).to(dtype)
+    x[:, vocab:] = float("nan")
+    tgt, _ = oracle.argmax(x, vocab)
+    draft_rows, _ = oracle.ragged_rows(cu)
+    plan = torch.where(torch.rand(total, generator=g) < p_copy, 1, 0)
+    plan = torch.where(torch.rand(total, generator=g) < 0.05, -1, plan)
+    uni = torch.randint(0, vocab, (total,), generator=g, dtype=torch.int64).to(torch.int32)
+    drafts = workloads.compose_drafts(tgt[draft_rows.long()][None, :], plan[None, :].to(torch.int8),
+                                      uni[None, :])[0]
+    return x, vocab, w, s, cu, drafts
+
+
+@pytest.mark.parametrize("seed,vocab,s,n_req,kmax", [(1, 1000, 3, 7, 4), (2, 50257, 3, 13, 6),
+                                                     (3, 200064, 4, 24, 5), (4, 997, 8, 40, 0),
+                                                     (5, 2000, 2, 1, 40)])
+def test_ragged_verify(seed, vocab, s, n_req, kmax):
+    """Per-request draft counts (some zero): row lists, one statistics launch for
+    both row lists, and the ragged finish, against the oracle."""
+    x_cpu, v, w, s, cu, drafts = _ragged_case(seed, vocab, s, n_req, kmax)
+    _announce(f"ragged V={v} S={s} R={n_req} Kmax={kmax} total={int(cu[-1])}")
+    want = oracle.greedy_verify_ragged(x_cpu, v, cu, drafts)
+    draft_rows, bonus_rows = oracle.ragged_rows(cu)
+    want_d = oracle.block_stats(x_cpu, v, w, s, 8192, rows=draft_rows)
+    want_b = oracle.block_stats(x_cpu, v, w, s, 1024, rows=bonus_rows)
+    want_s = oracle.greedy_verify_ragged_stats(want_d, want_b, cu, drafts)
+    for a, b in zip(want, want_s):
+        assert torch.equal(a, b)
+    x, cud, dd = _dev(x_cpu), _dev(cu), _dev(drafts)
+    total = int(cu[-1])
+    dr, br = vpa.ragged_rows(cud, total)
+    assert_same(dr, draft_rows, "draft rows")
+    assert_same(br, bonus_rows, "bonus rows")
+    dst, bst = vpa.verify_stats_rows(x, v, w, s, dr, br, 8192, 1024)
+    assert_same(dst, want_d, "ragged draft stats")
+    assert_same(bst, want_b, "ragged bonus stats")
+    got = vpa.greedy_verify_ragged(dst, bst, cud, dd, total)
+    for g, wv, nm in zip(got, want, ("out_tokens", "num_sampled", "num_rejected", "target_ids")):
+        assert_same(g, wv, f"ragged {nm}")
+    got2 = vpa.verify_ragged(x, v, w, s, cud, dd, total, with_targets=False)
+    for g, wv in zip(got2[:3], want[:3]):
+        assert_same(g, wv, "verify_ragged")
+
+
+def test_ragged_malformed_offsets_are_flagged():
+    """Offsets that decrease or run past the total: that request reports -1
+    counts and writes no tokens; the others are unaffected."""
+    x_cpu, v, w, s, cu, drafts = _ragged_case(9, 1000, 2, 4, 3)
+    total = int(cu[-1])
+    bad = cu.clone()
+    bad[2] = total + 50                      # request 1 runs past, request 2 decreases
+    dst = vpa.block_stats(_dev(x_cpu), v, w, s, 8192, rows=_dev(torch.arange(total, dtype=torch.int32)))
+    bst = vpa.block_stats(_dev(x_cpu), v, w, s, 1024,
+                          rows=_dev(torch.arange(4, dtype=torch.int32)))
+    out, ns, nr, tg = vpa.greedy_verify_ragged(dst, bst, _dev(bad), _dev(drafts), total)
+    ns, nr = _host(ns), _host(nr)
+    assert ns[1] == -1 and nr[1] == -1 and ns[2] == -1 and nr[2] == -1
+    assert ns[0] >= 1 and ns[3] >= 1
+    dr, br = vpa.ragged_rows(_dev(bad), total)
+    assert _host(br)[1:3].tolist() == [-1, -1]
+
+
 def test_row_list_out_of_range_rows_are_empty():
     case = workloads.edge_cases()[3]                      # vocab 1000, 8 shards, bf16
     x = _dev(case.logits)

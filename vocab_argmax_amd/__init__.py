@@ -34,8 +34,9 @@ DRAFT_BLOCK = 8192   # global block size for draft positions (PR #62604, "Purpos
 BONUS_BLOCK = 1024   # global block size for the bonus position
 
 # Every symbol include/vpa.h declares.
-SYMBOLS = ("vpa_stats_slots", "vpa_block_stats", "vpa_verify_stats", "vpa_combine_stats",
-           "vpa_top_tokens_workspace", "vpa_top_tokens", "vpa_greedy_verify", "vpa_last_error")
+SYMBOLS = ("vpa_stats_slots", "vpa_block_stats", "vpa_verify_stats", "vpa_verify_stats_rows",
+           "vpa_ragged_rows", "vpa_combine_stats", "vpa_top_tokens_workspace", "vpa_top_tokens",
+           "vpa_greedy_verify", "vpa_greedy_verify_ragged", "vpa_last_error")
 
 
 class VpaError(RuntimeError):
@@ -78,6 +79,14 @@ def _bind(lib):
     lib.vpa_top_tokens.restype = st
     lib.vpa_greedy_verify.argtypes = [vp, i32, vp, i32, i32, i64, i32, vp, vp, vp, vp, vp, vp]
     lib.vpa_greedy_verify.restype = st
+    lib.vpa_verify_stats_rows.argtypes = [vp, ctypes.c_int, i64, Vocab, i32, i32, vp, i64, vp, i64,
+                                          i64, i32, i32, vp, vp, vp]
+    lib.vpa_verify_stats_rows.restype = st
+    lib.vpa_ragged_rows.argtypes = [vp, i64, i64, vp, vp, vp]
+    lib.vpa_ragged_rows.restype = st
+    lib.vpa_greedy_verify_ragged.argtypes = [vp, i32, vp, i32, i32, i64, vp, i64, vp, vp, vp, vp,
+                                             vp, vp]
+    lib.vpa_greedy_verify_ragged.restype = st
     lib.vpa_last_error.argtypes = []
     lib.vpa_last_error.restype = ctypes.c_char_p
     return lib
@@ -307,3 +316,83 @@ def greedy_verify(draft_stats, bonus_stats, draft_ids, with_targets=True, out=No
                                    bonus_stats.shape[2], s, r, k, _vp(draft_ids), _vp(out_t),
                                    _vp(ns), _vp(nr), _vp(tg), _stream(stream)))
     return out_t, ns, nr, tg
+
+
+def _total_drafts(cu, total_drafts):
+    _int32_dev(cu, "cu", cu.device)
+    if cu.dim() != 1 or cu.numel() < 1:
+        raise ValueError("cu must be a 1-D int32 tensor of n_req+1 cumulative draft counts")
+    # reading cu[-1] synchronises with the device; callers that know the total pass it
+    return int(cu[-1]) if total_drafts is None else int(total_drafts)
+
+
+def ragged_rows(cu, total_drafts=None, stream=None):
+    """Row lists of a ragged verification batch from cumulative draft counts
+    cu [R+1]: (draft_rows int32[total_drafts], bonus_rows int32[R])."""
+    total = _total_drafts(cu, total_drafts)
+    n_req = cu.numel() - 1
+    draft_rows = torch.empty(total, dtype=torch.int32, device=cu.device)
+    bonus_rows = torch.empty(n_req, dtype=torch.int32, device=cu.device)
+    _check(lib().vpa_ragged_rows(_vp(cu), n_req, total, _vp(draft_rows), _vp(bonus_rows),
+                                 _stream(stream)))
+    return draft_rows, bonus_rows
+
+
+def verify_stats_rows(logits, vocab, shard_width, n_shards, draft_rows, bonus_rows,
+                      block_draft=DRAFT_BLOCK, block_bonus=BONUS_BLOCK, first_shard=0,
+                      n_local=None, stream=None):
+    """Draft- and bonus-row statistics for two explicit row lists in one launch:
+    (draft_stats [n_local][len(draft_rows)][Md][2], bonus_stats [n_local][len(bonus_rows)][Mb][2])."""
+    ld = _logits_ld(logits)
+    if n_local is None:
+        n_local = n_shards - first_shard
+    _int32_dev(draft_rows, "draft_rows", logits.device)
+    _int32_dev(bonus_rows, "bonus_rows", logits.device)
+    md = stats_slots(shard_width, n_shards, block_draft)
+    mb = stats_slots(shard_width, n_shards, block_bonus)
+    dst = torch.empty((n_local, draft_rows.numel(), md, 2), dtype=torch.int32, device=logits.device)
+    bst = torch.empty((n_local, bonus_rows.numel(), mb, 2), dtype=torch.int32, device=logits.device)
+    _check(lib().vpa_verify_stats_rows(_vp(logits), _dtype_code(logits), ld,
+                                       Vocab(vocab, shard_width, n_shards), first_shard, n_local,
+                                       _vp(draft_rows), draft_rows.numel(), _vp(bonus_rows),
+                                       bonus_rows.numel(), logits.shape[0], block_draft,
+                                       block_bonus, _vp(dst), _vp(bst), _stream(stream)))
+    return dst, bst
+
+
+def greedy_verify_ragged(draft_stats, bonus_stats, cu, draft_ids, total_drafts=None,
+                         with_targets=True, stream=None):
+    """Ragged greedy verification from statistics.  cu int32 [R+1] cumulative
+    draft counts; draft_ids int32 [total_drafts].  Returns (out_tokens
+    [total+R], num_sampled [R], num_rejected [R], target_ids [total+R] or None);
+    request r's K_r+1 outputs sit at offset cu[r]+r."""
+    _stats_tensor(draft_stats, "draft_stats")
+    _stats_tensor(bonus_stats, "bonus_stats")
+    total = _total_drafts(cu, total_drafts)
+    n_req = cu.numel() - 1
+    dev = bonus_stats.device
+    _int32_dev(draft_ids, "draft_ids", dev)
+    if draft_ids.numel() != total or draft_stats.shape[1] != total or bonus_stats.shape[1] != n_req:
+        raise ValueError("statistics / draft_ids do not match the offsets")
+    if draft_stats.shape[0] != bonus_stats.shape[0]:
+        raise ValueError("draft and bonus statistics have different shard counts")
+    out = torch.empty(total + n_req, dtype=torch.int32, device=dev)
+    ns = torch.empty(n_req, dtype=torch.int32, device=dev)
+    nr = torch.empty(n_req, dtype=torch.int32, device=dev)
+    tg = torch.empty(total + n_req, dtype=torch.int32, device=dev) if with_targets else None
+    _check(lib().vpa_greedy_verify_ragged(_vp(draft_stats), draft_stats.shape[2], _vp(bonus_stats),
+                                          bonus_stats.shape[2], bonus_stats.shape[0], n_req,
+                                          _vp(cu), total, _vp(draft_ids), _vp(out), _vp(ns),
+                                          _vp(nr), _vp(tg), _stream(stream)))
+    return out, ns, nr, tg
+
+
+def verify_ragged(logits, vocab, shard_width, n_shards, cu, draft_ids, total_drafts=None,
+                  block_draft=DRAFT_BLOCK, block_bonus=BONUS_BLOCK, with_targets=True,
+                  stream=None):
+    """The whole ragged verification on one GPU: row lists, statistics, finish."""
+    total = _total_drafts(cu, total_drafts)
+    draft_rows, bonus_rows = ragged_rows(cu, total, stream=stream)
+    dst, bst = verify_stats_rows(logits, vocab, shard_width, n_shards, draft_rows, bonus_rows,
+                                 block_draft, block_bonus, stream=stream)
+    return greedy_verify_ragged(dst, bst, cu, draft_ids, total, with_targets, stream=stream)

@@ -239,6 +239,62 @@ vpa_status vpa_verify_stats(const void* logits, vpa_dtype dtype, int64_t ld, vpa
     return e == hipSuccess ? ok() : hip_fail(e, "vpa_verify_stats launch");
 }
 
+vpa_status vpa_verify_stats_rows(const void* logits, vpa_dtype dtype, int64_t ld, vpa_vocab v,
+                                 int32_t first_shard, int32_t n_local_shards,
+                                 const int32_t* draft_rows, int64_t n_draft_rows,
+                                 const int32_t* bonus_rows, int64_t n_bonus_rows,
+                                 int64_t logits_rows, int32_t block_draft, int32_t block_bonus,
+                                 vpa_stat* draft_stats, vpa_stat* bonus_stats, void* stream) {
+    vpa::SegTask td, tb;
+    vpa_status st;
+    if ((st = check_logits_task(logits, dtype, ld, v, first_shard, n_local_shards, block_draft,
+                                td)) != VPA_OK)
+        return st;
+    if ((st = check_logits_task(logits, dtype, ld, v, first_shard, n_local_shards, block_bonus,
+                                tb)) != VPA_OK)
+        return st;
+    if (n_draft_rows < 0 || n_bonus_rows < 0 || logits_rows < 0)
+        return fail(VPA_ERR_INVALID, "negative row count");
+    if ((st = set_items(td, n_draft_rows, "vpa_verify_stats_rows (draft rows)")) != VPA_OK)
+        return st;
+    if ((st = set_items(tb, n_bonus_rows, "vpa_verify_stats_rows (bonus rows)")) != VPA_OK)
+        return st;
+    if ((int64_t)td.n_items + tb.n_items > INT32_MAX)
+        return fail(VPA_ERR_INVALID, "vpa_verify_stats_rows: too many statistics per call");
+    if (n_draft_rows == 0 && n_bonus_rows == 0)
+        return ok();
+    if ((st = check_logits_ptr(logits, dtype)) != VPA_OK)
+        return st;
+    if ((n_draft_rows && (!draft_rows || !aligned(draft_rows, 4) || !draft_stats ||
+                          !aligned(draft_stats, 8))) ||
+        (n_bonus_rows && (!bonus_rows || !aligned(bonus_rows, 4) || !bonus_stats ||
+                          !aligned(bonus_stats, 8))))
+        return fail(VPA_ERR_INVALID, "row list or statistics NULL or misaligned");
+    td.rows = draft_rows;
+    td.logits_rows = logits_rows;
+    td.stats = draft_stats;
+    tb.rows = bonus_rows;
+    tb.logits_rows = logits_rows;
+    tb.stats = bonus_stats;
+    hipError_t e = vpa::launch_block_stats(esize_of(dtype), td, tb, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "vpa_verify_stats_rows launch");
+}
+
+vpa_status vpa_ragged_rows(const int32_t* cu, int64_t n_req, int64_t total_drafts,
+                           int32_t* draft_rows, int32_t* bonus_rows, void* stream) {
+    if (n_req < 0 || total_drafts < 0 || total_drafts + n_req > INT32_MAX)
+        return fail(VPA_ERR_INVALID, "n_req %lld / total_drafts %lld out of range",
+                    (long long)n_req, (long long)total_drafts);
+    if (n_req == 0)
+        return ok();
+    if (!cu || !bonus_rows || (total_drafts && !draft_rows) || !aligned(cu, 4) ||
+        !aligned(bonus_rows, 4) || (draft_rows && !aligned(draft_rows, 4)))
+        return fail(VPA_ERR_INVALID, "cu/draft_rows/bonus_rows NULL or not 4-byte aligned");
+    hipError_t e = vpa::launch_ragged_rows(cu, (int32_t)n_req, (int32_t)total_drafts, draft_rows,
+                                           bonus_rows, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "vpa_ragged_rows launch");
+}
+
 vpa_status vpa_combine_stats(const vpa_stat* stats, int32_t n_shards, int64_t n_rows, int32_t m,
                              const vpa_epilogue* epi, int32_t* ids, uint32_t* val_bits,
                              int64_t* mapped, void* stream) {
@@ -332,6 +388,36 @@ vpa_status vpa_greedy_verify(const vpa_stat* draft_stats, int32_t m_draft,
                                              (int32_t)n_req, k, draft_ids, out_tokens, num_sampled,
                                              num_rejected, target_ids, (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "vpa_greedy_verify launch");
+}
+
+vpa_status vpa_greedy_verify_ragged(const vpa_stat* draft_stats, int32_t m_draft,
+                                    const vpa_stat* bonus_stats, int32_t m_bonus,
+                                    int32_t n_shards, int64_t n_req, const int32_t* cu,
+                                    int64_t total_drafts, const int32_t* draft_ids,
+                                    int32_t* out_tokens, int32_t* num_sampled,
+                                    int32_t* num_rejected, int32_t* target_ids, void* stream) {
+    if (n_shards < 1 || m_draft < 1 || m_bonus < 1 || (int64_t)n_shards * m_draft > INT32_MAX ||
+        (int64_t)n_shards * m_bonus > INT32_MAX)
+        return fail(VPA_ERR_INVALID, "n_shards %d / m_draft %d / m_bonus %d invalid",
+                    (int)n_shards, (int)m_draft, (int)m_bonus);
+    if (n_req < 0 || total_drafts < 0 || total_drafts + n_req > INT32_MAX)
+        return fail(VPA_ERR_INVALID, "n_req %lld / total_drafts %lld out of range",
+                    (long long)n_req, (long long)total_drafts);
+    if (n_req == 0)
+        return ok();
+    if (!cu || !bonus_stats || !out_tokens || !num_sampled || !num_rejected ||
+        (total_drafts && (!draft_stats || !draft_ids)))
+        return fail(VPA_ERR_INVALID, "a required pointer is NULL");
+    if (!aligned(cu, 4) || !aligned(bonus_stats, 8) || (draft_stats && !aligned(draft_stats, 8)) ||
+        (draft_ids && !aligned(draft_ids, 4)) || !aligned(out_tokens, 4) ||
+        !aligned(num_sampled, 4) || !aligned(num_rejected, 4) ||
+        (target_ids && !aligned(target_ids, 4)))
+        return fail(VPA_ERR_INVALID, "a pointer is misaligned");
+    hipError_t e = vpa::launch_greedy_verify_ragged(
+        draft_stats, m_draft, bonus_stats, m_bonus, n_shards, (int32_t)n_req, cu,
+        (int32_t)total_drafts, draft_ids, out_tokens, num_sampled, num_rejected, target_ids,
+        (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "vpa_greedy_verify_ragged launch");
 }
 
 const char* vpa_last_error(void) {

@@ -127,7 +127,98 @@ __global__ __launch_bounds__(kVerifyMaxThreads) void greedy_verify_kernel(
     }
 }
 
+// Ragged batch: one thread per request writes its row indices.  Every
+// index is checked against the buffers, so malformed offsets cannot write
+// out of bounds.
+__global__ __launch_bounds__(kThreads) void ragged_rows_kernel(const int32_t* __restrict__ cu,
+                                                               int32_t n_req, int32_t total,
+                                                               int32_t* __restrict__ draft_rows,
+                                                               int32_t* __restrict__ bonus_rows) {
+    const int32_t r = (int32_t)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (r >= n_req)
+        return;
+    const int32_t lo = cu[r], hi = cu[r + 1];
+    const bool ok = 0 <= lo && lo <= hi && hi <= total;
+    bonus_rows[r] = ok ? hi + r : -1;
+    if (!ok)
+        return;
+    for (int32_t i = lo; i < hi; ++i)
+        draft_rows[i] = i + r;
+}
+
+// Ragged verification: one workgroup per request r with K_r = cu[r+1]-cu[r]
+// drafts; the wavefronts share out the K_r+1 positions as in the uniform
+// kernel, then one lane applies the acceptance and writes K_r+1 outputs at
+// offset cu[r]+r.
+__global__ __launch_bounds__(kThreads) void greedy_verify_ragged_kernel(
+    const vpa_stat* __restrict__ draft_stats, int32_t m_draft,
+    const vpa_stat* __restrict__ bonus_stats, int32_t m_bonus, int32_t n_shards, int32_t n_req,
+    const int32_t* __restrict__ cu, int32_t total, const int32_t* __restrict__ draft_ids,
+    int32_t* __restrict__ out_tokens, int32_t* __restrict__ num_sampled,
+    int32_t* __restrict__ num_rejected, int32_t* __restrict__ target_ids) {
+    __shared__ int32_t targets[VPA_MAX_DRAFTS + 1];
+    const int lane = threadIdx.x & 63;
+    const int32_t wave = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
+    const int32_t r = (int32_t)blockIdx.x;
+    const int32_t lo = cu[r], hi = cu[r + 1];
+    const int32_t k = hi - lo;
+    if (!(0 <= lo && lo <= hi && hi <= total && k <= VPA_MAX_DRAFTS)) {
+        if (threadIdx.x == 0) {
+            num_sampled[r] = -1;
+            num_rejected[r] = -1;
+        }
+        return;   // uniform for the workgroup: no barrier is skipped by part of it
+    }
+    const int64_t base = (int64_t)lo + r;
+    for (int32_t j = wave; j <= k; j += kWaves) {
+        int32_t tgt;
+        uint32_t bits;
+        if (j < k)
+            row_best(draft_stats, n_shards, total, (int64_t)lo + j, m_draft, lane, tgt, bits);
+        else
+            row_best(bonus_stats, n_shards, n_req, r, m_bonus, lane, tgt, bits);
+        if (lane == 0) {
+            targets[j] = tgt;
+            if (target_ids)
+                target_ids[base + j] = tgt;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int32_t* drafts = draft_ids + lo;
+        int32_t n = 0;
+        while (n < k && drafts[n] == targets[n])
+            ++n;
+        for (int32_t j = 0; j <= k; ++j)
+            out_tokens[base + j] = j < n ? drafts[j] : (j == n ? targets[j] : -1);
+        num_sampled[r] = n + 1;
+        num_rejected[r] = k - n;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_ragged_rows(const int32_t* cu, int32_t n_req, int32_t total_drafts,
+                              int32_t* draft_rows, int32_t* bonus_rows, hipStream_t stream) {
+    const dim3 grid((unsigned)((n_req + kThreads - 1) / kThreads));
+    hipLaunchKernelGGL(ragged_rows_kernel, grid, dim3(kThreads), 0, stream, cu, n_req,
+                       total_drafts, draft_rows, bonus_rows);
+    return hipGetLastError();
+}
+
+hipError_t launch_greedy_verify_ragged(const vpa_stat* draft_stats, int32_t m_draft,
+                                       const vpa_stat* bonus_stats, int32_t m_bonus,
+                                       int32_t n_shards, int32_t n_req, const int32_t* cu,
+                                       int32_t total_drafts, const int32_t* draft_ids,
+                                       int32_t* out_tokens, int32_t* num_sampled,
+                                       int32_t* num_rejected, int32_t* target_ids,
+                                       hipStream_t stream) {
+    hipLaunchKernelGGL(greedy_verify_ragged_kernel, dim3((unsigned)n_req), dim3(kThreads), 0,
+                       stream, draft_stats, m_draft, bonus_stats, m_bonus, n_shards, n_req, cu,
+                       total_drafts, draft_ids, out_tokens, num_sampled, num_rejected,
+                       target_ids);
+    return hipGetLastError();
+}
 
 hipError_t launch_combine(const vpa_stat* stats, int32_t n_shards, int32_t n_rows, int32_t m,
                           const int64_t* d2t, int64_t d2t_len, float scale, int32_t* ids,
