@@ -272,6 +272,21 @@ def main():
         },
         "cpu_baseline": None,
     }
+    # the small configurations of the pages' workloads (latency-bound; reported only)
+    small = {}
+    w2 = workloads.config2(device=dev)
+    x2 = w2.logits
+    small["top_tokens_32x151936_s2"] = timed(
+        lambda: vpa.top_tokens(x2, w2.vocab, w2.shard_width, w2.n_shards, 8192), n_k)[1] / n_k * 1e6
+    w3 = workloads.config3(device=dev)
+    x3 = w3.logits
+    d3 = torch.zeros((w3.n_req, w3.k), dtype=torch.int32, device=dev)
+
+    def verify3():
+        st = vpa.verify_stats(x3, w3.vocab, w3.shard_width, w3.n_shards, w3.n_req, w3.k)
+        vpa.greedy_verify(st[0], st[1], d3, with_targets=False)
+    small["verify_24x4_rows_200064_s4"] = timed(verify3, n_k)[1] / n_k * 1e6
+    result["small_configs_us"] = small
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         torch.cuda.synchronize()

@@ -337,6 +337,31 @@ def test_config4_full_size_4096_rows():
                  w.name)
 
 
+def test_fp32_1024_rows_full_vocab():
+    """fp32 at scale: 1024 x 200064 fp32 (0.8 GB), 8 shards, top_tokens and the
+    verification statistics, every output against the oracle."""
+    g = torch.Generator().manual_seed(77)
+    v, w, s = 200064, 25008, 8
+    x_cpu = torch.randn((1024, v), generator=g) * 3
+    x_cpu[7, 199999] = float("nan")
+    x_cpu[9, :] = float("-inf")
+    x_cpu[11, 25007] = 50.0
+    x_cpu[11, 25008] = 50.0
+    _announce("fp32 1024 x 200064")
+    want_ids, want_vals = oracle.argmax(x_cpu, v)
+    x = _dev(x_cpu)
+    ids, vals = vpa.top_tokens(x, v, w, s, 8192)
+    assert_same(ids, want_ids, "fp32 ids")
+    assert_same(vals.to(torch.int64) & 0xFFFFFFFF, want_vals, "fp32 vals")
+    assert int(_host(ids)[11]) == 25007
+    n_req, k = 170, 5
+    plan = torch.ones((n_req, k), dtype=torch.int8)
+    plan[::3, 2] = 0
+    uni = torch.zeros((n_req, k), dtype=torch.int32)
+    drafts = workloads.compose_drafts(want_ids[:n_req * (k + 1)].reshape(n_req, k + 1), plan, uni)
+    _verify_both(x_cpu, v, w, s, n_req, k, drafts, 8192, 1024, "fp32 verify")
+
+
 def test_repeat_runs_are_bitwise_identical():
     w = workloads.config2()
     x = _dev(w.logits)
