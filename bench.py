@@ -286,6 +286,21 @@ def main():
         st = vpa.verify_stats(x3, w3.vocab, w3.shard_width, w3.n_shards, w3.n_req, w3.k)
         vpa.greedy_verify(st[0], st[1], d3, with_targets=False)
     small["verify_24x4_rows_200064_s4"] = timed(verify3, n_k)[1] / n_k * 1e6
+    # the same two calls captured once in a HIP graph and replayed: GPU time
+    # without the Python launch cost (a decode loop would replay like this)
+    ws2 = torch.empty(vpa.top_tokens_workspace(w2.vocab, w2.shard_width, w2.n_shards, 32),
+                      dtype=torch.uint8, device=dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        verify3()
+        vpa.top_tokens(x2, w2.vocab, w2.shard_width, w2.n_shards, 8192, workspace=ws2)
+    torch.cuda.current_stream().wait_stream(side)
+    g_small = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_small):
+        vpa.top_tokens(x2, w2.vocab, w2.shard_width, w2.n_shards, 8192, workspace=ws2)
+        verify3()
+    small["graph_top_tokens_32_plus_verify_24x4"] = timed(g_small.replay, n_k)[1] / n_k * 1e6
     result["small_configs_us"] = small
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)

@@ -374,6 +374,48 @@ def test_repeat_runs_are_bitwise_identical():
         assert torch.equal(st0, vpa.block_stats(x, w.vocab, w.shard_width, w.n_shards, 1024))
 
 
+def test_hip_graph_replays_match_eager():
+    """The draft argmax and the verification captured in one HIP graph: every
+    replay, with new logits copied in and eager work and synchronisation in
+    between, equals the eager calls on the same data (and the oracle)."""
+    w = workloads.config3()
+    v, wd, s, r, k = w.vocab, w.shard_width, w.n_shards, w.n_req, w.k
+    x_static = _dev(w.logits).clone()
+    drafts_static = torch.zeros((r, k), dtype=torch.int32, device=DEV)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):                      # warm the allocator off the default stream
+        vpa.top_tokens(x_static, v, wd, s, 8192)
+        vpa.greedy_verify(*vpa.verify_stats(x_static, v, wd, s, r, k), drafts_static)
+    torch.cuda.current_stream().wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g_ids, g_vals = vpa.top_tokens(x_static, v, wd, s, 8192)
+        dst, bst = vpa.verify_stats(x_static, v, wd, s, r, k)
+        g_out = vpa.greedy_verify(dst, bst, drafts_static)
+    for rep in range(4):
+        g = torch.Generator().manual_seed(600 + rep)
+        x_cpu = (torch.randn(w.logits.shape, generator=g) * 3).to(torch.bfloat16)
+        tgt, _ = oracle.argmax(x_cpu, v)
+        plan = (torch.rand((r, k), generator=g) < 0.6).to(torch.int8)
+        drafts = workloads.compose_drafts(tgt.reshape(r, k + 1), plan,
+                                          torch.zeros((r, k), dtype=torch.int32))
+        x_static.copy_(_dev(x_cpu))
+        drafts_static.copy_(_dev(drafts))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        e_ids, e_vals = vpa.top_tokens(x_static, v, wd, s, 8192)       # eager, same data
+        e_out = vpa.greedy_verify(*vpa.verify_stats(x_static, v, wd, s, r, k), drafts_static)
+        torch.cuda.synchronize()
+        assert torch.equal(g_ids, e_ids) and torch.equal(g_vals, e_vals), rep
+        for a, b in zip(g_out, e_out):
+            assert torch.equal(a, b), rep
+        want = oracle.greedy_verify_logits(x_cpu, v, drafts)
+        for a, b in zip(g_out, want):
+            assert_same(a, b, f"graph replay {rep} vs oracle")
+
+
 def test_empty_batch_gpu():
     x = torch.empty((0, 1000), dtype=torch.bfloat16, device=DEV)
     st = vpa.block_stats(x, 1000, 125, 8, 256)
