@@ -221,3 +221,29 @@ def test_ragged_rejects(lib):
     assert gr(FAKE, 7, FAKE, 50, 4, 3, FAKE, 6, FAKE, FAKE, FAKE, FAKE, FAKE_ODD, None) == vpa.VPA_ERR_INVALID
     assert gr(FAKE, 7, FAKE, 50, 4, -2, FAKE, 6, FAKE, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
     assert gr(None, 7, None, 50, 4, 0, None, 0, None, None, None, None, None, None) == vpa.VPA_OK
+
+
+def test_launches_beyond_one_dispatch_are_rejected(lib):
+    # A dispatch holds fewer than 2^32 work-items: calls whose statistics fit in
+    # 2^31 but whose launch would not are rejected before any HIP call.
+    big = (1 << 26) + 1                          # one 64-lane wavefront per row at V=16384
+    assert call_block_stats(lib, voc=V(16384, 16384, 1), ld=16384, block=16384, n_rows=big,
+                            logits_rows=big) == vpa.VPA_ERR_INVALID
+    assert "dispatch" in vpa.last_error()
+    assert lib.vpa_combine_stats(FAKE, 1, big, 1, None, FAKE, None, None, None) == vpa.VPA_ERR_INVALID
+    assert "dispatch" in vpa.last_error()
+    ws = vpa.lib().vpa_top_tokens_workspace(V(16384, 16384, 1), big, 16384)
+    assert lib.vpa_top_tokens(FAKE, vpa.VPA_BF16, 16384, V(16384, 16384, 1), big, 16384, FAKE, ws,
+                              None, FAKE, None, None, None) == vpa.VPA_ERR_INVALID
+    assert "dispatch" in vpa.last_error()
+    assert lib.vpa_verify_stats(FAKE, vpa.VPA_BF16, 16384, V(16384, 16384, 1), 0, 1, big // 2 + 1, 1,
+                                16384, 16384, FAKE, FAKE, None) == vpa.VPA_ERR_INVALID
+    assert "dispatch" in vpa.last_error()
+    req = (1 << 22) + 1                          # 16 wavefronts per request at K=15
+    assert lib.vpa_greedy_verify(FAKE, 1, FAKE, 1, 1, req, 15, FAKE, FAKE, FAKE, FAKE, None,
+                                 None) == vpa.VPA_ERR_INVALID
+    assert "dispatch" in vpa.last_error()
+    req = (1 << 24) + 1                          # one 256-thread workgroup per request
+    assert lib.vpa_greedy_verify_ragged(FAKE, 1, FAKE, 1, 1, req, FAKE, 0, None, FAKE, FAKE, FAKE,
+                                        None, None) == vpa.VPA_ERR_INVALID
+    assert "dispatch" in vpa.last_error()

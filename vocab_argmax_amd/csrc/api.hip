@@ -73,9 +73,8 @@ vpa_status check_dtype(vpa_dtype dt) {
 }
 
 // Shared checks of the logits-reading calls; fills `t` with the geometry.
-vpa_status check_logits_task(const void* logits, vpa_dtype dt, int64_t ld, const vpa_vocab& v,
-                             int32_t first_shard, int32_t n_local, int32_t block,
-                             vpa::SegTask& t) {
+vpa_status check_logits_task(vpa_dtype dt, int64_t ld, const vpa_vocab& v, int32_t first_shard,
+                             int32_t n_local, int32_t block, vpa::SegTask& t) {
     vpa_status st;
     if ((st = check_dtype(dt)) != VPA_OK)
         return st;
@@ -96,7 +95,6 @@ vpa_status check_logits_task(const void* logits, vpa_dtype dt, int64_t ld, const
         return fail(VPA_ERR_INVALID, "ld %lld < %lld valid local columns", (long long)ld,
                     (long long)need);
     t = vpa::SegTask{};
-    t.base = (const unsigned char*)logits;
     t.ld = ld;
     t.vocab = v.vocab;
     t.shard_width = v.shard_width;
@@ -149,6 +147,13 @@ vpa_status check_epilogue(const vpa_epilogue* epi, int64_t min_len, int64_t* map
     return ok();
 }
 
+vpa_status check_dispatch(int64_t threads, const char* what) {
+    if (threads > vpa::kMaxDispatchThreads)
+        return fail(VPA_ERR_INVALID, "%s: %lld work-items exceed one dispatch (2^32 - 1)", what,
+                    (long long)threads);
+    return ok();
+}
+
 vpa_status set_items(vpa::SegTask& t, int64_t n_rows, const char* what) {
     const int64_t items = n_rows * t.n_local * (int64_t)t.m;
     if (n_rows > INT32_MAX || items > INT32_MAX)
@@ -173,7 +178,7 @@ vpa_status vpa_block_stats(const void* logits, vpa_dtype dtype, int64_t ld, vpa_
                            int64_t n_rows, int64_t logits_rows, int32_t block, vpa_stat* stats,
                            void* stream) {
     vpa::SegTask t;
-    vpa_status st = check_logits_task(logits, dtype, ld, v, first_shard, n_local_shards, block, t);
+    vpa_status st = check_logits_task(dtype, ld, v, first_shard, n_local_shards, block, t);
     if (st != VPA_OK)
         return st;
     if (n_rows < 0)
@@ -190,10 +195,14 @@ vpa_status vpa_block_stats(const void* logits, vpa_dtype dtype, int64_t ld, vpa_
         return fail(VPA_ERR_INVALID, "stats is NULL or not 8-byte aligned");
     if (rows && !aligned(rows, 4))
         return fail(VPA_ERR_INVALID, "rows not 4-byte aligned");
+    t.base = (const unsigned char*)logits;
     t.rows = rows;
     t.logits_rows = logits_rows;
     t.stats = stats;
     vpa::SegTask none{};
+    if ((st = check_dispatch(vpa::block_stats_threads(esize_of(dtype), t, none),
+                             "vpa_block_stats")) != VPA_OK)
+        return st;
     hipError_t e = vpa::launch_block_stats(esize_of(dtype), t, none, (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "vpa_block_stats launch");
 }
@@ -204,11 +213,9 @@ vpa_status vpa_verify_stats(const void* logits, vpa_dtype dtype, int64_t ld, vpa
                             vpa_stat* bonus_stats, void* stream) {
     vpa::SegTask td, tb;
     vpa_status st;
-    if ((st = check_logits_task(logits, dtype, ld, v, first_shard, n_local_shards, block_draft,
-                                td)) != VPA_OK)
+    if ((st = check_logits_task(dtype, ld, v, first_shard, n_local_shards, block_draft, td)) != VPA_OK)
         return st;
-    if ((st = check_logits_task(logits, dtype, ld, v, first_shard, n_local_shards, block_bonus,
-                                tb)) != VPA_OK)
+    if ((st = check_logits_task(dtype, ld, v, first_shard, n_local_shards, block_bonus, tb)) != VPA_OK)
         return st;
     if (k < 1 || k > VPA_MAX_DRAFTS)
         return fail(VPA_ERR_INVALID, "k %d outside [1, %d]", (int)k, VPA_MAX_DRAFTS);
@@ -227,6 +234,7 @@ vpa_status vpa_verify_stats(const void* logits, vpa_dtype dtype, int64_t ld, vpa
     if (!draft_stats || !bonus_stats || !aligned(draft_stats, 8) || !aligned(bonus_stats, 8))
         return fail(VPA_ERR_INVALID, "draft_stats/bonus_stats NULL or not 8-byte aligned");
     const int64_t logits_rows = n_req * (int64_t)(k + 1);
+    td.base = tb.base = (const unsigned char*)logits;
     td.row_k = k;
     td.row_bonus = 0;
     td.logits_rows = logits_rows;
@@ -235,6 +243,9 @@ vpa_status vpa_verify_stats(const void* logits, vpa_dtype dtype, int64_t ld, vpa
     tb.row_bonus = 1;
     tb.logits_rows = logits_rows;
     tb.stats = bonus_stats;
+    if ((st = check_dispatch(vpa::block_stats_threads(esize_of(dtype), td, tb),
+                             "vpa_verify_stats")) != VPA_OK)
+        return st;
     hipError_t e = vpa::launch_block_stats(esize_of(dtype), td, tb, (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "vpa_verify_stats launch");
 }
@@ -247,11 +258,9 @@ vpa_status vpa_verify_stats_rows(const void* logits, vpa_dtype dtype, int64_t ld
                                  vpa_stat* draft_stats, vpa_stat* bonus_stats, void* stream) {
     vpa::SegTask td, tb;
     vpa_status st;
-    if ((st = check_logits_task(logits, dtype, ld, v, first_shard, n_local_shards, block_draft,
-                                td)) != VPA_OK)
+    if ((st = check_logits_task(dtype, ld, v, first_shard, n_local_shards, block_draft, td)) != VPA_OK)
         return st;
-    if ((st = check_logits_task(logits, dtype, ld, v, first_shard, n_local_shards, block_bonus,
-                                tb)) != VPA_OK)
+    if ((st = check_logits_task(dtype, ld, v, first_shard, n_local_shards, block_bonus, tb)) != VPA_OK)
         return st;
     if (n_draft_rows < 0 || n_bonus_rows < 0 || logits_rows < 0)
         return fail(VPA_ERR_INVALID, "negative row count");
@@ -270,12 +279,16 @@ vpa_status vpa_verify_stats_rows(const void* logits, vpa_dtype dtype, int64_t ld
         (n_bonus_rows && (!bonus_rows || !aligned(bonus_rows, 4) || !bonus_stats ||
                           !aligned(bonus_stats, 8))))
         return fail(VPA_ERR_INVALID, "row list or statistics NULL or misaligned");
+    td.base = tb.base = (const unsigned char*)logits;
     td.rows = draft_rows;
     td.logits_rows = logits_rows;
     td.stats = draft_stats;
     tb.rows = bonus_rows;
     tb.logits_rows = logits_rows;
     tb.stats = bonus_stats;
+    if ((st = check_dispatch(vpa::block_stats_threads(esize_of(dtype), td, tb),
+                             "vpa_verify_stats_rows")) != VPA_OK)
+        return st;
     hipError_t e = vpa::launch_block_stats(esize_of(dtype), td, tb, (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "vpa_verify_stats_rows launch");
 }
@@ -312,6 +325,8 @@ vpa_status vpa_combine_stats(const vpa_stat* stats, int32_t n_shards, int64_t n_
         return fail(VPA_ERR_INVALID, "stats is NULL or not 8-byte aligned");
     if (!ids || !aligned(ids, 4) || (val_bits && !aligned(val_bits, 4)))
         return fail(VPA_ERR_INVALID, "ids is NULL, or ids/val_bits not 4-byte aligned");
+    if ((st = check_dispatch(vpa::combine_threads((int32_t)n_rows), "vpa_combine_stats")) != VPA_OK)
+        return st;
     hipError_t he = vpa::launch_combine(stats, n_shards, (int32_t)n_rows, m, e.d2t, e.d2t_len,
                                         e.scale, ids, val_bits, mapped, (hipStream_t)stream);
     return he == hipSuccess ? ok() : hip_fail(he, "vpa_combine_stats launch");
@@ -332,7 +347,7 @@ vpa_status vpa_top_tokens(const void* logits, vpa_dtype dtype, int64_t ld, vpa_v
                           const vpa_epilogue* epi, int32_t* ids, uint32_t* val_bits,
                           int64_t* mapped, void* stream) {
     vpa::SegTask t;
-    vpa_status st = check_logits_task(logits, dtype, ld, v, 0, v.n_shards, block, t);
+    vpa_status st = check_logits_task(dtype, ld, v, 0, v.n_shards, block, t);
     if (st != VPA_OK)
         return st;
     Epi ep;
@@ -351,9 +366,15 @@ vpa_status vpa_top_tokens(const void* logits, vpa_dtype dtype, int64_t ld, vpa_v
         return fail(VPA_ERR_INVALID, "workspace NULL, unaligned or smaller than %zu bytes", need);
     if (!ids || !aligned(ids, 4) || (val_bits && !aligned(val_bits, 4)))
         return fail(VPA_ERR_INVALID, "ids is NULL, or ids/val_bits not 4-byte aligned");
+    t.base = (const unsigned char*)logits;
     t.logits_rows = n_rows;
     t.stats = (vpa_stat*)workspace;
     vpa::SegTask none{};
+    if ((st = check_dispatch(vpa::block_stats_threads(esize_of(dtype), t, none),
+                             "vpa_top_tokens (statistics)")) != VPA_OK ||
+        (st = check_dispatch(vpa::combine_threads((int32_t)n_rows), "vpa_top_tokens (combine)")) !=
+            VPA_OK)
+        return st;
     hipError_t e = vpa::launch_block_stats(esize_of(dtype), t, none, (hipStream_t)stream);
     if (e != hipSuccess)
         return hip_fail(e, "vpa_top_tokens statistics launch");
@@ -384,6 +405,9 @@ vpa_status vpa_greedy_verify(const vpa_stat* draft_stats, int32_t m_draft,
     if (!aligned(draft_ids, 4) || !aligned(out_tokens, 4) || !aligned(num_sampled, 4) ||
         !aligned(num_rejected, 4) || (target_ids && !aligned(target_ids, 4)))
         return fail(VPA_ERR_INVALID, "an int32 array is not 4-byte aligned");
+    vpa_status st = check_dispatch(vpa::greedy_verify_threads((int32_t)n_req, k), "vpa_greedy_verify");
+    if (st != VPA_OK)
+        return st;
     hipError_t e = vpa::launch_greedy_verify(draft_stats, m_draft, bonus_stats, m_bonus, n_shards,
                                              (int32_t)n_req, k, draft_ids, out_tokens, num_sampled,
                                              num_rejected, target_ids, (hipStream_t)stream);
@@ -413,6 +437,10 @@ vpa_status vpa_greedy_verify_ragged(const vpa_stat* draft_stats, int32_t m_draft
         !aligned(num_sampled, 4) || !aligned(num_rejected, 4) ||
         (target_ids && !aligned(target_ids, 4)))
         return fail(VPA_ERR_INVALID, "a pointer is misaligned");
+    vpa_status st =
+        check_dispatch(vpa::greedy_verify_ragged_threads((int32_t)n_req), "vpa_greedy_verify_ragged");
+    if (st != VPA_OK)
+        return st;
     hipError_t e = vpa::launch_greedy_verify_ragged(
         draft_stats, m_draft, bonus_stats, m_bonus, n_shards, (int32_t)n_req, cu,
         (int32_t)total_drafts, draft_ids, out_tokens, num_sampled, num_rejected, target_ids,

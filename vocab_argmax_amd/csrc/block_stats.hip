@@ -316,14 +316,26 @@ int lanes_log2_for(const SegTask& t, int esize) {
 
 }  // namespace
 
-hipError_t launch_block_stats(int esize, const SegTask& t0_in, const SegTask& t1_in,
-                              hipStream_t stream) {
-    SegTask t0 = t0_in, t1 = t1_in;
+// Group sizes and wavefront counts of a launch over t0 then t1.
+void plan_block_stats(int esize, SegTask& t0, SegTask& t1) {
     for (SegTask* t : {&t0, &t1}) {
         t->lanes_log2 = lanes_log2_for(*t, esize);
         const int32_t per_wave = 1 << (6 - t->lanes_log2);
         t->n_waves = t->n_items > 0 ? (t->n_items + per_wave - 1) / per_wave : 0;
     }
+}
+
+int64_t block_stats_threads(int esize, const SegTask& t0_in, const SegTask& t1_in) {
+    SegTask t0 = t0_in, t1 = t1_in;
+    plan_block_stats(esize, t0, t1);
+    const int64_t waves = (int64_t)t0.n_waves + t1.n_waves;
+    return (waves + kWaves - 1) / kWaves * kThreads;
+}
+
+hipError_t launch_block_stats(int esize, const SegTask& t0_in, const SegTask& t1_in,
+                              hipStream_t stream) {
+    SegTask t0 = t0_in, t1 = t1_in;
+    plan_block_stats(esize, t0, t1);
     const int64_t waves = (int64_t)t0.n_waves + t1.n_waves;
     if (waves <= 0)
         return hipSuccess;

@@ -198,6 +198,19 @@ __global__ __launch_bounds__(kThreads) void greedy_verify_ragged_kernel(
 
 }  // namespace
 
+int64_t combine_threads(int32_t n_rows) {
+    return ((int64_t)n_rows + kWaves - 1) / kWaves * kThreads;
+}
+
+int64_t greedy_verify_threads(int32_t n_req, int32_t k) {
+    const int64_t waves = k + 1 < kVerifyMaxThreads / 64 ? k + 1 : kVerifyMaxThreads / 64;
+    return (int64_t)n_req * 64 * waves;
+}
+
+int64_t greedy_verify_ragged_threads(int32_t n_req) {
+    return (int64_t)n_req * kThreads;
+}
+
 hipError_t launch_ragged_rows(const int32_t* cu, int32_t n_req, int32_t total_drafts,
                               int32_t* draft_rows, int32_t* bonus_rows, hipStream_t stream) {
     const dim3 grid((unsigned)((n_req + kThreads - 1) / kThreads));

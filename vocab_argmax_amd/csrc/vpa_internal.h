@@ -40,6 +40,17 @@ struct SegTask {
 // of t1 (t1.n_items may be 0).  Both tasks share dtype `esize` (2 or 4).
 hipError_t launch_block_stats(int esize, const SegTask& t0, const SegTask& t1, hipStream_t stream);
 
+// Work-items that launch would use (a dispatch holds fewer than 2^32).
+int64_t block_stats_threads(int esize, const SegTask& t0, const SegTask& t1);
+
+// Work-items of the other launches, for the same check.
+int64_t combine_threads(int32_t n_rows);
+int64_t greedy_verify_threads(int32_t n_req, int32_t k);
+int64_t greedy_verify_ragged_threads(int32_t n_req);
+
+// Most work-items one dispatch may hold.
+constexpr int64_t kMaxDispatchThreads = ((int64_t)1 << 32) - 1;
+
 // Combine with the epilogue already validated: d2t may be null (then mapped
 // is null too); scale is finite and positive.
 hipError_t launch_combine(const vpa_stat* stats, int32_t n_shards, int32_t n_rows, int32_t m,
