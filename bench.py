@@ -21,9 +21,11 @@ Prints one JSON line: value = logits rows reduced per second (4096 + 4092
 rows per step), timed over exactly --steps steps between two
 synchronisations, after 50 ms of settling and the --warmup steps; roofline = the block-statistics kernel in the launch shape
 of vpa_verify_stats, whose average duration HIP events on the launch stream
-measure over back-to-back launches right after the timed steps, against
-MI355X's 8 TB/s HBM peak; cpu_baseline = the CPU oracle timed on this host on
-the same step.
+measure over back-to-back launches right after the timed steps (median of 5
+windows), against MI355X's 8 TB/s HBM peak; top_tokens_rows_sweep = the fused
+argmax alone at 1024, 2048 and 4096 bf16 rows and 1024 fp32 rows, alternating
+two input buffers; cpu_baseline = the CPU oracle timed on this host on the
+same step.
 """
 import argparse
 import hashlib
@@ -41,6 +43,8 @@ V, W, S = 200064, 25008, 8
 N_ROWS, K = 4096, 5
 R = N_ROWS // (K + 1)                       # 682 requests; rows 4092..4095 are not referenced
 B_DRAFT, B_BONUS = 8192, 1024
+F32_ROWS = 1024                             # fp32 leg: 2 x 1024 x 200064 x 4 B = 1.6 GB
+REPEATS = 5                                 # per-call timings: median of 5 windows
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_stats_bf16_v200064_traffic.json")
 KERNEL_SOURCES = ("vocab_argmax_amd/csrc/block_stats.hip", "vocab_argmax_amd/csrc/vpa_device.h")
 
@@ -105,11 +109,24 @@ def cpu_baseline(draft_cpu, target_cpu, drafts_cpu, gpu_out, min_seconds=10.0, m
               and torch.equal(ver[0], g_out) and torch.equal(ver[1], g_ns)
               and torch.equal(ver[2], g_nr))
     rows = reps * (N_ROWS + R * (K + 1))
+    step_bytes = sum(algorithmic_bytes().values())
     return {"value": rows / elapsed, "unit": "rows/s", "cores": 1, "kind": "oracle",
             "sample": f"{reps} full step(s): {N_ROWS} argmax rows + {R * (K + 1)} verification "
                       f"rows of the same workload, {elapsed:.1f} s, one thread pinned to one core"
-                      f" of {os.cpu_count()}",
+                      f" of {os.cpu_count()} ({cpu_model()})",
+            "gbps": reps * step_bytes / elapsed / 1e9,
             "parity_with_gpu_step": bool(parity)}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
 
 
 def main():
@@ -218,13 +235,43 @@ def main():
     for _ in range(args.warmup):
         step()
     wall, gpu = timed(step, args.steps)           # the timed region: exactly K steps
-    # per-call durations of each launch shape, back to back, same inputs
+    # per-call durations of each launch shape, back to back, same inputs: the
+    # median over REPEATS windows of n_k calls each
     n_k = max(args.steps, 10)
-    tt_s = timed(top, n_k)[1] / n_k
-    vs_s = timed(vstats, n_k)[1] / n_k
-    gv_s = timed(finish, n_k)[1] / n_k
-    te_s = timed(top_epilogue, n_k)[1] / n_k
-    rg_s = timed(ragged, n_k)[1] / n_k
+
+    def per_call(fn, n=n_k):
+        return sorted(timed(fn, n)[1] / n for _ in range(REPEATS))[REPEATS // 2]
+
+    tt_s = per_call(top)
+    vs_s = per_call(vstats)
+    gv_s = per_call(finish)
+    te_s = per_call(top_epilogue)
+    rg_s = per_call(ragged)
+
+    # top_tokens at 1024, 2048 and 4096 rows, alternating between the draft
+    # and target buffers so that consecutive calls never read the same rows
+    def rows_sweep(bufs, n_rows, esize):
+        m = slots(W, S, B_DRAFT)
+        wsn = torch.empty(vpa.top_tokens_workspace(V, W, S, n_rows, B_DRAFT), dtype=torch.uint8,
+                          device=dev)
+        idn = torch.empty(n_rows, dtype=torch.int32, device=dev)
+        vln = torch.empty(n_rows, dtype=torch.int32, device=dev)
+        views = [b[:n_rows] for b in bufs]
+        flip = [0]
+
+        def call():
+            vpa.top_tokens(views[flip[0]], V, W, S, B_DRAFT, workspace=wsn, ids=idn, val_bits=vln)
+            flip[0] ^= 1
+        t = per_call(call, 2 * n_k)
+        alg_b = n_rows * (V * esize + S * m * 8 * 2 + 8)
+        return {"us": t * 1e6, "rows_per_s": n_rows / t, "gbps": alg_b / t / 1e9,
+                "hbm_frac": alg_b / t / 1e9 / PEAK_HBM_GBPS}
+
+    sweep = {f"bf16_n{n}": rows_sweep((xd, xt), n, 2) for n in (1024, 2048, N_ROWS)}
+    f32_bufs = [workloads.config4(device=dev, n_rows=F32_ROWS, seed=seed,
+                                  dtype=torch.float32).logits for seed in (3004, 4004)]
+    sweep[f"fp32_n{F32_ROWS}"] = rows_sweep(f32_bufs, F32_ROWS, 4)
+    del f32_bufs
 
     ms_step = max(wall, gpu) * 1e3 / args.steps
     alg = algorithmic_bytes()
@@ -259,6 +306,7 @@ def main():
                     "greedy_verify": gv_s * 1e6, "top_tokens_d2t_scale": te_s * 1e6,
                     "verify_ragged_all_steps": rg_s * 1e6},
         "top_tokens_gbps": alg["top_tokens"] / tt_s / 1e9,
+        "top_tokens_rows_sweep": sweep,
         "roofline": {
             "kernel": "block_stats_kernel<bf16> (vpa_verify_stats launch)",
             "bound": "hbm",
@@ -276,8 +324,8 @@ def main():
     small = {}
     w2 = workloads.config2(device=dev)
     x2 = w2.logits
-    small["top_tokens_32x151936_s2"] = timed(
-        lambda: vpa.top_tokens(x2, w2.vocab, w2.shard_width, w2.n_shards, 8192), n_k)[1] / n_k * 1e6
+    small["top_tokens_32x151936_s2"] = per_call(
+        lambda: vpa.top_tokens(x2, w2.vocab, w2.shard_width, w2.n_shards, 8192)) * 1e6
     w3 = workloads.config3(device=dev)
     x3 = w3.logits
     d3 = torch.zeros((w3.n_req, w3.k), dtype=torch.int32, device=dev)
@@ -285,7 +333,7 @@ def main():
     def verify3():
         st = vpa.verify_stats(x3, w3.vocab, w3.shard_width, w3.n_shards, w3.n_req, w3.k)
         vpa.greedy_verify(st[0], st[1], d3, with_targets=False)
-    small["verify_24x4_rows_200064_s4"] = timed(verify3, n_k)[1] / n_k * 1e6
+    small["verify_24x4_rows_200064_s4"] = per_call(verify3) * 1e6
     # the same two calls captured once in a HIP graph and replayed: GPU time
     # without the Python launch cost (a decode loop would replay like this)
     ws2 = torch.empty(vpa.top_tokens_workspace(w2.vocab, w2.shard_width, w2.n_shards, 32),
@@ -300,7 +348,7 @@ def main():
     with torch.cuda.graph(g_small):
         vpa.top_tokens(x2, w2.vocab, w2.shard_width, w2.n_shards, 8192, workspace=ws2)
         verify3()
-    small["graph_top_tokens_32_plus_verify_24x4"] = timed(g_small.replay, n_k)[1] / n_k * 1e6
+    small["graph_top_tokens_32_plus_verify_24x4"] = per_call(g_small.replay) * 1e6
     result["small_configs_us"] = small
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)

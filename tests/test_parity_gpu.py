@@ -374,6 +374,25 @@ def test_repeat_runs_are_bitwise_identical():
         assert torch.equal(st0, vpa.block_stats(x, w.vocab, w.shard_width, w.n_shards, 1024))
 
 
+def test_top_tokens_workspace_reused_across_shapes():
+    """One workspace, filled with garbage once, serves calls of different
+    shapes, dtypes and block sizes in a row: its contents on entry do not
+    matter, and each call's outputs equal the oracle's."""
+    cases = [(c.logits, c.vocab, c.shard_width, c.n_shards, b, c.name)
+             for c in workloads.edge_cases()[:3] for b in c.blocks]
+    w2 = workloads.config2()
+    cases.insert(2, (w2.logits, w2.vocab, w2.shard_width, w2.n_shards, 8192, w2.name))
+    need = max(vpa.top_tokens_workspace(v, wd, s, x.shape[0], b) for x, v, wd, s, b, _ in cases)
+    g = torch.Generator().manual_seed(91)
+    ws = _dev(torch.randint(0, 256, (need,), generator=g, dtype=torch.int32).to(torch.uint8))
+    for x_cpu, v, wd, s, b, name in cases:
+        _announce(f"shared workspace: {name} block={b}")
+        want_ids, want_vals = oracle.argmax(x_cpu, v)
+        ids, vals = vpa.top_tokens(_dev(x_cpu), v, wd, s, b, workspace=ws)
+        assert_same(ids, want_ids, f"{name} B={b} ids")
+        assert_same(vals.to(torch.int64) & 0xFFFFFFFF, want_vals, f"{name} B={b} vals")
+
+
 def test_hip_graph_replays_match_eager():
     """The draft argmax and the verification captured in one HIP graph: every
     replay, with new logits copied in and eager work and synchronisation in

@@ -113,15 +113,19 @@ def config3(device="cpu") -> Workload:
     return Workload("verify_v200064_bf16_tp4_r24_k3", x, v, w, s, [8192, 1024], r, k, plan, uni)
 
 
-def config4(device="cpu", n_rows: int = 4096, seed: int = 1004) -> Workload:
+def config4(device="cpu", n_rows: int = 4096, seed: int = 1004,
+            dtype=torch.bfloat16) -> Workload:
     """n_rows x vocab 200064 bf16 ~N(0,3), 8 shards of 25008; verification of
     682 requests x (K=5 + 1) rows (the last 4 rows are not referenced), drafts copy
-    the target with p=0.4; blocks 8192 / 1024."""
+    the target with p=0.4; blocks 8192 / 1024.  dtype=torch.float32 gives the
+    same values uncast (the fp32 variant of the workload)."""
     v, w, s, k = 200064, 25008, 8, 5
     r = n_rows // (k + 1)
-    x = _normal_rows(n_rows, v, 3.0, seed=seed, device=device)
+    x = _normal_rows(n_rows, v, 3.0, seed=seed, device=device, dtype=dtype)
     plan, uni = _draft_plan(r, k, 0.4, v, seed=seed + 1000)
-    return Workload(f"stress_v200064_bf16_tp8_n{n_rows}", x, v, w, s, [8192, 1024], r, k, plan, uni)
+    tag = "fp32" if dtype == torch.float32 else "bf16"
+    return Workload(f"stress_v200064_{tag}_tp8_n{n_rows}", x, v, w, s, [8192, 1024], r, k, plan,
+                    uni)
 
 
 # ---------------------------------------------------------------------------
