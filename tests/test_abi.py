@@ -4,6 +4,8 @@ need no GPU; pointers passed here are never dereferenced)."""
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -247,3 +249,34 @@ def test_launches_beyond_one_dispatch_are_rejected(lib):
     assert lib.vpa_greedy_verify_ragged(FAKE, 1, FAKE, 1, 1, req, FAKE, 0, None, FAKE, FAKE, FAKE,
                                         None, None) == vpa.VPA_ERR_INVALID
     assert "dispatch" in vpa.last_error()
+
+
+def test_header_is_plain_c_and_cxx(tmp_path):
+    """include/vpa.h compiles as strict C99 and as C++11, warnings as errors."""
+    cc = shutil.which("gcc")
+    cxx = shutil.which("g++")
+    if not cc or not cxx:
+        pytest.skip("gcc/g++ not available")
+    src = tmp_path / "h.c"
+    src.write_text('#include "vpa.h"\nint main(void) { return 0; }\n')
+    inc = os.path.dirname(HEADER)
+    for cmd in ([cc, "-std=c99", "-pedantic"], [cxx, "-std=c++11", "-pedantic", "-x", "c++"]):
+        subprocess.run(cmd + ["-Wall", "-Wextra", "-Werror", "-I", inc, "-fsyntax-only", str(src)],
+                       check=True)
+
+
+def test_plain_c_program_links_and_calls(tmp_path):
+    """A C99 program links against the built library and gets host-side
+    answers (slots, workspace, rejections, empty batches) without a GPU."""
+    cc = shutil.which("gcc")
+    if not cc:
+        pytest.skip("gcc not available")
+    lib_dir = os.path.dirname(vpa.LIB_PATH)
+    exe = tmp_path / "c_consumer"
+    here = os.path.dirname(os.path.abspath(__file__))
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.dirname(HEADER),
+                    os.path.join(here, "c_consumer.c"), "-L", lib_dir, "-l:libvpa.so",
+                    f"-Wl,-rpath,{lib_dir}", "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert "FAIL" not in out.stdout and out.stdout.count("ok ") == 7, out.stdout

@@ -393,6 +393,43 @@ def test_top_tokens_workspace_reused_across_shapes():
         assert_same(vals.to(torch.int64) & 0xFFFFFFFF, want_vals, f"{name} B={b} vals")
 
 
+def test_two_streams_run_concurrently():
+    """The library keeps no device state between calls: two streams each run
+    the draft argmax and the verification on their own data, interleaved
+    call by call, and both match the oracle."""
+    w = workloads.config3()
+    v, wd, s, r, k = w.vocab, w.shard_width, w.n_shards, w.n_req, w.k
+    g = torch.Generator().manual_seed(4242)
+    xs = [w.logits, (torch.randn(w.logits.shape, generator=g) * 3).to(torch.bfloat16)]
+    drafts = []
+    for x_cpu in xs:
+        tgt, _ = oracle.argmax(x_cpu, v)
+        plan = (torch.rand((r, k), generator=g) < 0.5).to(torch.int8)
+        drafts.append(workloads.compose_drafts(tgt.reshape(r, k + 1), plan,
+                                               torch.zeros((r, k), dtype=torch.int32)))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    xd = [_dev(x) for x in xs]
+    dd = [_dev(d) for d in drafts]
+    torch.cuda.synchronize()
+    results = [[], []]
+    for _ in range(3):
+        for i in (0, 1):
+            with torch.cuda.stream(streams[i]):
+                ids, vals = vpa.top_tokens(xd[i], v, wd, s, 8192)
+                out = vpa.greedy_verify(*vpa.verify_stats(xd[i], v, wd, s, r, k), dd[i])
+                results[i].append((ids, vals) + tuple(out))
+    torch.cuda.synchronize()
+    for i in (0, 1):
+        _announce(f"stream {i}")
+        want_ids, want_vals = oracle.argmax(xs[i], v)
+        want = oracle.greedy_verify_logits(xs[i], v, drafts[i])
+        for got in results[i]:
+            assert_same(got[0], want_ids, f"stream {i} ids")
+            assert_same(got[1].to(torch.int64) & 0xFFFFFFFF, want_vals, f"stream {i} vals")
+            for a, b in zip(got[2:], want):
+                assert_same(a, b, f"stream {i} verification")
+
+
 def test_hip_graph_replays_match_eager():
     """The draft argmax and the verification captured in one HIP graph: every
     replay, with new logits copied in and eager work and synchronisation in
