@@ -241,7 +241,10 @@ vpa_status vpa_greedy_verify(const vpa_stat* draft_stats, int32_t m_draft,
  *  num_sampled, num_rejected  out, int32 [n_req]: accepted+1 and K_r-accepted;
  *               both -1 for a request whose offsets are malformed (K_r < 0,
  *               K_r > VPA_MAX_DRAFTS, or outside [0, total_drafts]), which then
- *               writes no tokens.
+ *               writes no tokens.  Offsets that pass these checks one by
+ *               one but decrease across requests make requests overlap:
+ *               their outputs are then unspecified, though every access
+ *               stays inside the arrays above.
  *  target_ids   out, int32 [total_drafts + n_req] or NULL. */
 vpa_status vpa_greedy_verify_ragged(const vpa_stat* draft_stats, int32_t m_draft,
                                     const vpa_stat* bonus_stats, int32_t m_bonus,

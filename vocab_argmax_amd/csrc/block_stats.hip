@@ -10,13 +10,15 @@
 // Work decomposition (CDNA4, wave64): a segment is scanned by a group of L
 // lanes of one wavefront (L = 64 for 8192-column bf16 blocks, down to 8 for
 // 1024-column ones), so a lane makes about 16 iterations of 16-byte
-// non-temporal loads whatever the block size, issued 8 at a time (8 KiB per
-// wavefront in flight); four wavefronts per workgroup, no LDS and no
-// barriers.  Chunks of 8 keep the kernel under 70 VGPRs, i.e. 7 wavefronts
-// per SIMD, which measured faster on MI355X than 16-deep chunks at 4.  Each lane keeps a running best, and a
-// shuffle reduction inside the group finishes the segment.  Consecutive
-// groups and wavefronts take consecutive segments of a row, so a wavefront
-// reads contiguous memory.  Padding columns [V, S*W) are never read.
+// non-temporal loads whatever the block size; four wavefronts per
+// workgroup, no LDS and no barriers.  The loads come in chunks of U group
+// iterations, software-pipelined: chunk c+1 is issued before chunk c is
+// folded, so a wavefront keeps U to 2U loads in flight.  U = 8 for bf16
+// (91 VGPRs, 5 wavefronts per SIMD) and 16 for fp32 measured fastest on
+// MI355X.  Each lane keeps a running best, and a shuffle reduction inside
+// the group finishes the segment.  Consecutive groups and wavefronts take
+// consecutive segments of a row, so a wavefront reads contiguous memory.
+// Padding columns [V, S*W) are never read.
 //
 // Per-lane scan.  Every element becomes an order-preserving unsigned key
 // (vpa_device.h); bf16 keys are 16 bits wide and computed two at a time with
@@ -41,19 +43,22 @@ namespace {
 #ifndef VPA_WAVES_PER_WG
 #define VPA_WAVES_PER_WG 4
 #endif
-#ifndef VPA_ITERS_PER_CHUNK
-#define VPA_ITERS_PER_CHUNK 8
+#ifndef VPA_PIPE_BF16
+#define VPA_PIPE_BF16 8
 #endif
-#ifndef VPA_NT_LOADS
-#define VPA_NT_LOADS 1
+#ifndef VPA_PIPE_F32
+#define VPA_PIPE_F32 16
 #endif
 #ifndef VPA_LANE_ITERS
 #define VPA_LANE_ITERS 16
 #endif
 constexpr int kWaves = VPA_WAVES_PER_WG;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kItersPerChunk = VPA_ITERS_PER_CHUNK;   // group iterations loaded together
 constexpr int kLaneIters = VPA_LANE_ITERS;   // target iterations per lane of a segment
+
+// Group iterations per pipelined chunk, by element size.
+template <int ESIZE>
+constexpr int kPipe = ESIZE == 2 ? VPA_PIPE_BF16 : VPA_PIPE_F32;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef const u32x4 __attribute__((address_space(1)))* gvec_ptr;
@@ -67,29 +72,32 @@ __device__ __forceinline__ void take_better(uint32_t& bk, int32_t& bc, uint32_t 
     }
 }
 
-// One chunk of U group iterations over the segment's full vectors seg[0, n):
-// the lane reads seg[i0 + L*u] for u < U, with i0 = (lane in group) + L*t0.
-// FULL: every such index is below n; otherwise indices are clamped to n-1,
-// which only re-reads that vector (a duplicate decodes to the same column, so
-// it cannot change the result).  Column of element e of seg[i] = c0 + i*VEC + e.
-template <int ESIZE, int L, int U, bool FULL>
-__device__ __forceinline__ void scan_chunk(gvec_ptr seg, uint32_t i0, uint32_t ilast, int32_t c0,
-                                           uint32_t& bk, int32_t& bc) {
-    u32x4 v[U];
+// The segment's full vectors seg[0, n), n >= 1, in chunks of U group
+// iterations: in chunk c the lane reads seg[i0 + L*u] for u < U, with
+// i0 = (lane in group) + L*U*c.  Indices past the end are clamped to n-1,
+// which only re-reads that vector (a duplicate decodes to the same column,
+// so it cannot change the result).  Column of element e of seg[i] =
+// c0 + i*VEC + e.
+template <int ESIZE, int L, int U>
+__device__ __forceinline__ void load_clamped(gvec_ptr seg, uint32_t i0, uint32_t ilast,
+                                             u32x4 (&v)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         uint32_t i = i0 + L * u;
-        if (!FULL)
-            i = i < ilast ? i : ilast;
-#if VPA_NT_LOADS
+        i = i < ilast ? i : ilast;
         v[u] = __builtin_nontemporal_load(seg + i);
-#else
-        v[u] = seg[i];
-#endif
     }
+}
+
+// Fold one loaded chunk (chunk origin i0) into the lane's running best.
+template <int ESIZE, int L, int U>
+__device__ __forceinline__ void fold_loaded(const u32x4 (&v)[U], uint32_t i0, uint32_t ilast,
+                                            int32_t c0, uint32_t& bk, int32_t& bc) {
     if constexpr (ESIZE == 2) {
-        // key16 << 16 | (0xFFFF - position): one unsigned max keeps the largest
-        // key and, among equal keys, the earliest position of this lane.
+        // key16 << 16 | (0xFFFF - position): one unsigned max keeps the
+        // largest key and, among equal keys, the earliest position of this
+        // lane.  v_perm_b32 picks bytes of {k, c}: selector 0x05040100 gives
+        // (k << 16) | c.lo16, 0x07060100 gives (k & 0xFFFF0000) | c.lo16.
         uint32_t best = 0;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -97,8 +105,6 @@ __device__ __forceinline__ void scan_chunk(gvec_ptr seg, uint32_t i0, uint32_t i
             for (int d = 0; d < 4; ++d) {
                 const uint32_t k = keys_bf16x2(v[u][d]);
                 const uint32_t pos = u * 8 + d * 2;
-                // v_perm_b32 picks bytes of {k, c}: selector 0x05040100 gives
-                // (k << 16) | c.lo16, 0x07060100 gives (k & 0xFFFF0000) | c.lo16.
                 const uint32_t lo = __builtin_amdgcn_perm(k, 0xFFFFu - pos, 0x05040100u);
                 const uint32_t hi = __builtin_amdgcn_perm(k, 0xFFFFu - (pos + 1), 0x07060100u);
                 best = max(best, max(lo, hi));
@@ -106,8 +112,7 @@ __device__ __forceinline__ void scan_chunk(gvec_ptr seg, uint32_t i0, uint32_t i
         }
         const uint32_t pos = 0xFFFFu - (best & 0xFFFFu);
         uint32_t i = i0 + L * (pos >> 3);
-        if (!FULL)
-            i = i < ilast ? i : ilast;
+        i = i < ilast ? i : ilast;
         take_better(bk, bc, best >> 16, c0 + (int32_t)(i * 8 + (pos & 7)));
     } else {
         uint32_t ck = 0, cpos = 0;
@@ -123,22 +128,28 @@ __device__ __forceinline__ void scan_chunk(gvec_ptr seg, uint32_t i0, uint32_t i
             }
         }
         uint32_t i = i0 + L * (cpos >> 2);
-        if (!FULL)
-            i = i < ilast ? i : ilast;
+        i = i < ilast ? i : ilast;
         take_better(bk, bc, ck, c0 + (int32_t)(i * 4 + (cpos & 3)));
     }
 }
 
-// Iterations [t0, t0+U) of the group.  The unclamped form is used only when
-// it is valid for every group of the wavefront, so the branch is uniform.
+// Chunk c+1's loads are issued before chunk c is folded.
 template <int ESIZE, int L, int U>
-__device__ __forceinline__ void scan_iters(gvec_ptr seg, uint32_t n, uint32_t t0, uint32_t gl,
-                                           int32_t c0, uint32_t& bk, int32_t& bc) {
-    const uint32_t i0 = gl + L * t0;
-    if (__all(L * (t0 + U) <= n))
-        scan_chunk<ESIZE, L, U, true>(seg, i0, n - 1, c0, bk, bc);
-    else
-        scan_chunk<ESIZE, L, U, false>(seg, i0, n - 1, c0, bk, bc);
+__device__ __forceinline__ void scan_pipelined(gvec_ptr seg, uint32_t n, uint32_t gl, int32_t c0,
+                                               uint32_t& bk, int32_t& bc) {
+    const uint32_t nit = (n + L - 1) / L;
+    const uint32_t chunks = (nit + U - 1) / U;
+    u32x4 a[U], b[U];
+    load_clamped<ESIZE, L, U>(seg, gl, n - 1, a);
+    for (uint32_t c = 0; c + 1 < chunks; ++c) {
+        const uint32_t i0 = gl + L * U * c;
+        load_clamped<ESIZE, L, U>(seg, i0 + L * U, n - 1, b);
+        fold_loaded<ESIZE, L, U>(a, i0, n - 1, c0, bk, bc);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            a[u] = b[u];
+    }
+    fold_loaded<ESIZE, L, U>(a, gl + L * U * (chunks - 1), n - 1, c0, bk, bc);
 }
 
 __device__ __forceinline__ uint32_t load_bits(const unsigned char* base, int esize, int64_t e) {
@@ -221,24 +232,8 @@ __device__ __forceinline__ void segment_stat(const SegTask& t, int32_t item, uin
         const gvec_ptr seg = (gvec_ptr)(base - (uintptr_t)(mis * ESIZE)) + qa;
         const uint32_t n = (uint32_t)(qb - qa);
         const int32_t c0 = (int32_t)(qa * VEC + D);
-        const uint32_t nit = (n + L - 1) / L;   // group iterations over full vectors
-        uint32_t t0 = 0;
-        for (; t0 + kItersPerChunk <= nit; t0 += kItersPerChunk)
-            scan_iters<ESIZE, L, kItersPerChunk>(seg, n, t0, gl, c0, bk, bc);
-        if (t0 + 8 <= nit) {
-            scan_iters<ESIZE, L, 8>(seg, n, t0, gl, c0, bk, bc);
-            t0 += 8;
-        }
-        if (t0 + 4 <= nit) {
-            scan_iters<ESIZE, L, 4>(seg, n, t0, gl, c0, bk, bc);
-            t0 += 4;
-        }
-        if (t0 + 2 <= nit) {
-            scan_iters<ESIZE, L, 2>(seg, n, t0, gl, c0, bk, bc);
-            t0 += 2;
-        }
-        if (t0 < nit)
-            scan_iters<ESIZE, L, 1>(seg, n, t0, gl, c0, bk, bc);
+        if (n > 0)
+            scan_pipelined<ESIZE, L, kPipe<ESIZE>>(seg, n, gl, c0, bk, bc);
     }
 
     group_best_key_col<L>(bk, bc);
@@ -302,7 +297,7 @@ void block_stats_kernel(SegTask t0, SegTask t1) {
         task_wave<ESIZE>(t1, wave, lane);
 }
 
-// Lanes per segment: about kItersPerChunk 16-byte vectors per lane for the
+// Lanes per segment: about kLaneIters 16-byte vectors per lane for the
 // longest segment, between 8 lanes (128 contiguous bytes per group load) and
 // the full wavefront.
 int lanes_log2_for(const SegTask& t, int esize) {
