@@ -362,6 +362,36 @@ def test_fp32_1024_rows_full_vocab():
     _verify_both(x_cpu, v, w, s, n_req, k, drafts, 8192, 1024, "fp32 verify")
 
 
+def test_row_offsets_beyond_4gb():
+    """64-bit addressing: rows 1.2e9 elements apart (2.4 GB of bf16), so row 2
+    starts 4.8 GB into the buffer, past 2^31 elements and 2^32 bytes.  Only
+    the first V columns of each row are filled and read."""
+    v, w, s, ld = 200064, 25008, 8, 1_200_000_000
+    g = torch.Generator().manual_seed(4096)
+    x_cpu = (torch.randn((3, v), generator=g) * 3).to(torch.bfloat16)
+    x_cpu[2, 199_000] = 40.0
+    x_cpu[1, 5] = float("nan")
+    _announce("3 rows, ld = 1.2e9 (7.2 GB buffer)")
+    big = torch.empty((3, ld), dtype=torch.bfloat16, device=DEV)
+    big[:, :v] = _dev(x_cpu)
+    x = big[:, :v]
+    assert x.stride(0) == ld
+    want_ids, want_vals = oracle.argmax(x_cpu, v)
+    ids, vals = vpa.top_tokens(x, v, w, s, 8192)
+    assert_same(ids, want_ids, "ids beyond 4 GB")
+    assert_same(vals.to(torch.int64) & 0xFFFFFFFF, want_vals, "vals beyond 4 GB")
+    assert _host(ids).tolist()[1:] == [5, 199_000]
+    rows = torch.tensor([2, 0, 2, 1], dtype=torch.int32)
+    st = vpa.block_stats(x, v, w, s, 1024, rows=_dev(rows))
+    assert_same(st, oracle.block_stats(x_cpu, v, w, s, 1024, rows=rows), "row-list stats")
+    drafts = torch.tensor([[int(want_ids[0]), 7]], dtype=torch.int32)
+    got = vpa.greedy_verify(*vpa.verify_stats(x, v, w, s, 1, 2), _dev(drafts))
+    for a, b in zip(got, oracle.greedy_verify_logits(x_cpu, v, drafts)):
+        assert_same(a, b, "verification beyond 4 GB")
+    del big, x
+    torch.cuda.empty_cache()
+
+
 def test_repeat_runs_are_bitwise_identical():
     w = workloads.config2()
     x = _dev(w.logits)
