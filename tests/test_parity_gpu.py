@@ -287,8 +287,9 @@ def test_random_geometries():
 
 
 def test_long_segments_and_chunk_cascade():
-    """Blocks far larger than 16 wave iterations (the chunk loop) and every
-    remainder size of the 8/4/2/1 cascade, with ties planted far apart."""
+    """Blocks far larger than one pipelined chunk (many chunks per segment),
+    segments that end part-way through a chunk, and ties planted far
+    apart."""
     for dtype in (torch.bfloat16, torch.float32):
         for vocab, s, block in ((200064, 2, 1 << 20), (200064, 1, 1 << 21), (131071, 3, 65536),
                                 (9000, 1, 9000), (5000, 1, 4608)):
@@ -302,6 +303,26 @@ def test_long_segments_and_chunk_cascade():
             x[2, vocab - 1] = float("nan")
             x[3, :vocab] = float("-inf")
             check_stats_and_ids(x, vocab, w, s, block, f"long V={vocab} S={s} B={block} {dtype}")
+
+
+def test_largest_vocabulary():
+    """V = 2^24 - 1, the largest the boundary accepts, over 8 shards of
+    2^21 columns: ids up to 2^24 - 2, one padding column, both dtypes and
+    both block sizes of the pages."""
+    v, s = (1 << 24) - 1, 8
+    w = -(-v // s)
+    for dtype in (torch.bfloat16, torch.float32):
+        g = torch.Generator().manual_seed(24)
+        x = (torch.randn((3, s * w), generator=g) * 3).to(dtype)
+        x[:, v:] = float("inf")
+        x[0, v - 1] = 50.0
+        x[1, v - 1] = float("nan")
+        x[2, 0] = 50.0
+        x[2, v - 1] = 50.0
+        for block in (8192, 1024):
+            check_stats_and_ids(x, v, w, s, block, f"V=2^24-1 {dtype}")
+        ids, _ = vpa.top_tokens(_dev(x), v, w, s, 8192)
+        assert _host(ids).tolist() == [v - 1, v - 1, 0]
 
 
 def test_config2_top_tokens_v151936_bf16_tp2():
