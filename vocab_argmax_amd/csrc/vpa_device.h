@@ -75,35 +75,52 @@ __device__ __forceinline__ uint32_t bits_of_key_bf16(uint32_t k) {
     return h << 16;
 }
 
-// Wave-wide lexicographic maximum of (key, -column): afterwards every lane
-// holds the largest key and, among equal keys, the lowest column.  Start a
-// lane with nothing as (0, INT32_MAX).
-__device__ __forceinline__ void wave_best_key_col(uint32_t& key, int32_t& col) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const uint32_t ok = __shfl_xor(key, off, 64);
-        const int32_t oc = __shfl_xor(col, off, 64);
-        if (ok > key || (ok == key && oc < col)) {
-            key = ok;
-            col = oc;
-        }
-    }
+// Cross-lane reductions with DPP lane moves (no LDS round trips).  A step
+// moves a value from a partner lane within the same row of 16 lanes
+// (quad_perm, row_half_mirror, row_mirror) or broadcasts the last lane of
+// a row into the next rows (row_bcast:15, row_bcast:31).  Rows left out by
+// row_mask keep their own value, so combining it with itself is a no-op.
+// After all six steps, lane 63 holds the wavefront's result.
+namespace dpp {
+constexpr int kSwap1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kSwap2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141; // lane i <-> 7-i within 8
+constexpr int kMirror = 0x140;     // lane i <-> 15-i within 16
+constexpr int kBcast15 = 0x142;    // lane 15 of a row -> the next row
+constexpr int kBcast31 = 0x143;    // lane 31 -> rows 2 and 3
+}  // namespace dpp
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
 }
 
-// Same, carrying the winner's value bits along; `nid` is the bitwise NOT of
-// the token id, so a larger nid means a lower id.
+// One step of the maximum of (key, nid) carrying the winner's value bits;
+// `nid` is the bitwise NOT of the token id, so a larger nid is a lower id.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void stat_step(uint32_t& key, uint32_t& nid, uint32_t& bits) {
+    const uint32_t ok = dpp_move<CTRL, ROW_MASK>(key);
+    const uint32_t on = dpp_move<CTRL, ROW_MASK>(nid);
+    const uint32_t ob = dpp_move<CTRL, ROW_MASK>(bits);
+    const bool take = ok > key || (ok == key && on > nid);
+    key = take ? ok : key;
+    nid = take ? on : nid;
+    bits = take ? ob : bits;
+}
+
+// Wave-wide maximum of (key, nid) with the winner's bits; afterwards every
+// lane holds the result.  Start a lane with nothing as (0, 0, any bits).
+// Every lane of the wavefront must be active.
 __device__ __forceinline__ void wave_best_stat(uint32_t& key, uint32_t& nid, uint32_t& bits) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const uint32_t ok = __shfl_xor(key, off, 64);
-        const uint32_t on = __shfl_xor(nid, off, 64);
-        const uint32_t ob = __shfl_xor(bits, off, 64);
-        if (ok > key || (ok == key && on > nid)) {
-            key = ok;
-            nid = on;
-            bits = ob;
-        }
-    }
+    stat_step<dpp::kSwap1, 0xF>(key, nid, bits);
+    stat_step<dpp::kSwap2, 0xF>(key, nid, bits);
+    stat_step<dpp::kHalfMirror, 0xF>(key, nid, bits);
+    stat_step<dpp::kMirror, 0xF>(key, nid, bits);
+    stat_step<dpp::kBcast15, 0xA>(key, nid, bits);
+    stat_step<dpp::kBcast31, 0xC>(key, nid, bits);
+    key = __builtin_amdgcn_readlane(key, 63);
+    nid = __builtin_amdgcn_readlane(nid, 63);
+    bits = __builtin_amdgcn_readlane(bits, 63);
 }
 
 }  // namespace vpa
