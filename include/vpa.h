@@ -84,12 +84,13 @@ typedef struct {
 #define VPA_EMPTY_ID 0x7FFFFFFF
 #define VPA_MAX_VOCAB (1 << 24) /* the vocabulary must stay below this */
 #define VPA_MAX_DRAFTS 4096     /* most draft tokens per request (K) */
+#define VPA_MAX_SHARDS (1 << 24) /* most vocabulary shards (S) */
 
 /* Vocabulary geometry: V valid columns, S shards of W columns each. */
 typedef struct {
     int64_t vocab;       /* V, 1 <= V < 2^24 */
     int64_t shard_width; /* W >= 1 */
-    int32_t n_shards;    /* S >= 1, S*W >= V (a shard may hold only padding) */
+    int32_t n_shards;    /* 1 <= S <= VPA_MAX_SHARDS, S*W >= V (a shard may hold only padding) */
 } vpa_vocab;
 
 /* Optional epilogue of the combined argmax k of a row.
@@ -112,7 +113,8 @@ typedef struct {
  * [b*block, (b+1)*block) that any shard [s*W, (s+1)*W), s < S, touches
  * (PR #62604, "Purpose" item 1: global block boundaries across shard edges).
  * Slot j of shard s is block floor(s*W/block)+j cut to the shard and to
- * [0, V).  Returns -1 on invalid arguments (W < 1, S < 1, block < 1). */
+ * [0, V).  Returns -1 on invalid arguments (W < 1, S < 1, S > VPA_MAX_SHARDS,
+ * block < 1) or when M would not fit an int32. */
 int32_t vpa_stats_slots(int64_t shard_width, int32_t n_shards, int32_t block);
 
 /* Per-block statistics of the local shards (PR #62604, "Purpose" item 1;

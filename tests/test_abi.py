@@ -280,3 +280,20 @@ def test_plain_c_program_links_and_calls(tmp_path):
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert out.returncode == 0, out.stdout + out.stderr
     assert "FAIL" not in out.stdout and out.stdout.count("ok ") == 7, out.stdout
+
+
+def test_sizes_past_the_limits_are_rejected_without_overflow(lib):
+    """Shard counts above 2^24 and row counts near 2^63 are rejected at once:
+    the host checks never loop over absurd shard counts or overflow."""
+    assert lib.vpa_stats_slots(1, (1 << 24) + 1, 1) == -1
+    assert lib.vpa_stats_slots(1, 1 << 24, 1 << 30) == 1
+    assert call_block_stats(lib, voc=V(1000, 1, (1 << 24) + 1)) == vpa.VPA_ERR_INVALID
+    assert "n_shards" in vpa.last_error()
+    huge = (1 << 62) + 3
+    assert lib.vpa_top_tokens_workspace(V(1000, 1000, 1), huge, 256) == 0
+    assert lib.vpa_top_tokens_workspace(V(1000, 1000, 1), 1 << 31, 256) == 0
+    assert call_block_stats(lib, n_rows=huge, logits_rows=huge) == vpa.VPA_ERR_INVALID
+    assert lib.vpa_top_tokens(FAKE, vpa.VPA_BF16, 1000, V(1000, 125, 8), huge, 256, FAKE, 1 << 40,
+                              None, FAKE, None, None, None) == vpa.VPA_ERR_INVALID
+    assert lib.vpa_verify_stats(FAKE, vpa.VPA_BF16, 1000, V(1000, 125, 8), 0, 8, huge, 3, 8192,
+                                1024, FAKE, FAKE, None) == vpa.VPA_ERR_INVALID

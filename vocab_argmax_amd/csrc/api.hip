@@ -40,8 +40,9 @@ bool aligned(const void* p, size_t a) {
 }
 
 // Slots per shard M (the most global blocks any shard touches), -1 if invalid.
+// At most VPA_MAX_SHARDS shards, so the scan below stays short.
 int64_t slots(int64_t w, int64_t s, int64_t b) {
-    if (w < 1 || s < 1 || b < 1)
+    if (w < 1 || s < 1 || s > VPA_MAX_SHARDS || b < 1)
         return -1;
     int64_t m = 0;
     for (int64_t i = 0; i < s; ++i) {
@@ -58,8 +59,9 @@ vpa_status check_vocab(const vpa_vocab& v) {
         return fail(VPA_ERR_INVALID, "vocab %lld outside [1, 2^24)", (long long)v.vocab);
     if (v.shard_width < 1 || v.shard_width > INT32_MAX)
         return fail(VPA_ERR_INVALID, "shard_width %lld outside [1, 2^31)", (long long)v.shard_width);
-    if (v.n_shards < 1)
-        return fail(VPA_ERR_INVALID, "n_shards %d < 1", (int)v.n_shards);
+    if (v.n_shards < 1 || v.n_shards > VPA_MAX_SHARDS)
+        return fail(VPA_ERR_INVALID, "n_shards %d outside [1, %d]", (int)v.n_shards,
+                    (int)VPA_MAX_SHARDS);
     if ((int64_t)v.n_shards * v.shard_width < v.vocab)
         return fail(VPA_ERR_INVALID, "n_shards*shard_width = %lld does not cover vocab %lld",
                     (long long)((int64_t)v.n_shards * v.shard_width), (long long)v.vocab);
@@ -155,10 +157,14 @@ vpa_status check_dispatch(int64_t threads, const char* what) {
 }
 
 vpa_status set_items(vpa::SegTask& t, int64_t n_rows, const char* what) {
-    const int64_t items = n_rows * t.n_local * (int64_t)t.m;
-    if (n_rows > INT32_MAX || items > INT32_MAX)
-        return fail(VPA_ERR_INVALID, "%s: %lld statistics exceed 2^31-1 per call", what,
-                    (long long)items);
+    if (n_rows > INT32_MAX)
+        return fail(VPA_ERR_INVALID, "%s: %lld rows exceed 2^31-1 per call", what,
+                    (long long)n_rows);
+    const int64_t per_row = (int64_t)t.n_local * t.m;   // < 2^24 * 2^31
+    if (per_row > INT32_MAX || n_rows > INT32_MAX / per_row)
+        return fail(VPA_ERR_INVALID, "%s: %lld rows x %lld statistics exceed 2^31-1 per call",
+                    what, (long long)n_rows, (long long)per_row);
+    const int64_t items = n_rows * per_row;
     t.n_rows = (int32_t)n_rows;
     t.n_items = (int32_t)items;
     return ok();
@@ -333,13 +339,19 @@ vpa_status vpa_combine_stats(const vpa_stat* stats, int32_t n_shards, int64_t n_
 }
 
 size_t vpa_top_tokens_workspace(vpa_vocab v, int64_t n_rows, int32_t block) {
-    if (n_rows <= 0 || v.vocab < 1 || v.vocab >= VPA_MAX_VOCAB || v.n_shards < 1 ||
-        v.shard_width < 1 || (int64_t)v.n_shards * v.shard_width < v.vocab)
+    if (n_rows <= 0 || n_rows > INT32_MAX || v.vocab < 1 || v.vocab >= VPA_MAX_VOCAB ||
+        v.n_shards < 1 || v.n_shards > VPA_MAX_SHARDS || v.shard_width < 1 ||
+        v.shard_width > INT32_MAX || (int64_t)v.n_shards * v.shard_width < v.vocab)
         return 0;
     const int64_t m = slots(v.shard_width, v.n_shards, block);
     if (m < 1)
         return 0;
-    return (size_t)(v.n_shards * n_rows * m) * sizeof(vpa_stat);
+    // A call is limited to 2^31-1 statistics; larger sizes get 0 (and the
+    // products below cannot overflow: S < 2^25 and M < 2^32).
+    const int64_t per_row = (int64_t)v.n_shards * m;
+    if (per_row > INT32_MAX || n_rows > INT32_MAX / per_row)
+        return 0;
+    return (size_t)(per_row * n_rows) * sizeof(vpa_stat);
 }
 
 vpa_status vpa_top_tokens(const void* logits, vpa_dtype dtype, int64_t ld, vpa_vocab v,
