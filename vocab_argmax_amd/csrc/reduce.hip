@@ -10,7 +10,7 @@
 // Statistics arrive in rank order, [S][rows][M].  One wavefront reduces one
 // row (a combine row, or one position of a verified request): lanes stride
 // over the row's S*M statistics, keep the best under the argmax order (key of
-// the value bits, then the lower id), and a shuffle reduction finishes.  The lexicographic
+// the value bits, then the lower id), and a DPP cross-lane reduction finishes.  The lexicographic
 // (key, -id) maximum is order independent, so the result equals a scan in
 // rank order that keeps only strictly better statistics; an empty slot
 // (-inf, id INT32_MAX) loses to every real statistic.
