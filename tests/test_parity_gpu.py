@@ -357,6 +357,32 @@ def test_config4_full_size_4096_rows():
     _verify_both(w.logits, w.vocab, w.shard_width, w.n_shards, w.n_req, w.k, drafts, 8192, 1024,
                  w.name)
 
+    # the epilogue call the benchmark times: a 200064-entry table, scale 1/0.7
+    _announce(f"{w.name}: epilogue")
+    g = torch.Generator().manual_seed(4004)
+    d2t = torch.randint(0, 1000, (w.vocab,), generator=g, dtype=torch.int64)
+    ids, vals, mapped = vpa.top_tokens(x, w.vocab, w.shard_width, w.n_shards, 8192, d2t=_dev(d2t),
+                                       scale=1 / 0.7)
+    assert_same(ids, want_ids, "config4 epilogue ids")
+    assert_same(vals.to(torch.int64) & 0xFFFFFFFF, oracle.scale_bits(want_vals, 1 / 0.7),
+                "config4 epilogue values")
+    assert_same(mapped, oracle.map_ids(want_ids, d2t), "config4 epilogue mapped ids")
+
+    # the ragged batch the benchmark times: K_r = 7r mod 11 drafts over 682
+    # requests (3410 drafts, rows 0..4091), drafts copying their target with p = 1/2
+    _announce(f"{w.name}: ragged verification")
+    ks = [(7 * r) % 11 for r in range(w.n_req)]
+    cu = torch.tensor([0] + [sum(ks[:r + 1]) for r in range(w.n_req)], dtype=torch.int32)
+    total = int(cu[-1])
+    tgt = torch.cat([want_ids[int(cu[r]) + r:int(cu[r + 1]) + r] for r in range(w.n_req)])
+    keep = torch.rand(total, generator=g) < 0.5
+    drafts_r = torch.where(keep, tgt, torch.randint(0, w.vocab, (total,), generator=g,
+                                                    dtype=torch.int64).to(torch.int32))
+    want = oracle.greedy_verify_ragged(w.logits, w.vocab, cu, drafts_r)
+    got = vpa.verify_ragged(x, w.vocab, w.shard_width, w.n_shards, _dev(cu), _dev(drafts_r), total)
+    for a, b, nm in zip(got, want, ("out_tokens", "num_sampled", "num_rejected", "target_ids")):
+        assert_same(a, b, f"config4 ragged {nm}")
+
 
 def test_fp32_1024_rows_full_vocab():
     """fp32 at scale: 1024 x 200064 fp32 (0.8 GB), 8 shards, top_tokens and the
