@@ -269,6 +269,29 @@ def _random_case(rng, trial):
     return full, off, vocab, w, s, block
 
 
+def test_draft_model_vocab_40960_k15():
+    """The smallest vocabulary the pages name (40960, a draft model's, in
+    PR #39419, "Current Issue") at TP2 and TP4, with K = 15 drafts per
+    request as in their DFlash runs: statistics, argmax and verification."""
+    v = 40960
+    g = torch.Generator().manual_seed(40960)
+    x = (torch.randn((64, v), generator=g) * 3).to(torch.bfloat16)
+    x[3, 20479] = 30.0                        # a tie across the TP2 shard edge
+    x[3, 20480] = 30.0
+    for s in (2, 4):
+        w = v // s
+        for block in (8192, 1024):
+            check_stats_and_ids(x, v, w, s, block, f"V=40960 S={s}")
+        n_req, k = 4, 15
+        tgt, _ = oracle.argmax(x, v)
+        plan = (torch.rand((n_req, k), generator=g) < 0.8).to(torch.int8)
+        drafts = workloads.compose_drafts(tgt.reshape(n_req, k + 1), plan,
+                                          torch.randint(0, v, (n_req, k), generator=g,
+                                                        dtype=torch.int64).to(torch.int32))
+        _verify_both(x, v, w, s, n_req, k, drafts, 8192, 1024, f"V=40960 S={s} K=15")
+    assert int(_host(vpa.top_tokens(_dev(x), v, v // 2, 2, 8192)[0])[3]) == 20479
+
+
 def test_random_geometries():
     """Random V, S, W, block, dtype, row padding and base misalignment."""
     rng = random.Random(1234)
