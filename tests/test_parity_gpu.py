@@ -530,6 +530,29 @@ def test_two_streams_run_concurrently():
                 assert_same(a, b, f"stream {i} verification")
 
 
+def test_explicit_stream_argument():
+    """Every call accepts an explicit torch stream: work enqueued on a side
+    stream, synchronised on that stream alone, matches the oracle."""
+    w = workloads.config3()
+    v, wd, s, r, k = w.vocab, w.shard_width, w.n_shards, w.n_req, w.k
+    x = _dev(w.logits)
+    tgt, vals = oracle.argmax(w.logits, v)
+    drafts = workloads.compose_drafts(tgt.reshape(r, k + 1), w.draft_plan, w.draft_uniform)
+    dd = _dev(drafts)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    ids, vb = vpa.top_tokens(x, v, wd, s, 8192, stream=side)
+    st = vpa.block_stats(x, v, wd, s, 8192, stream=side)
+    ids2, _ = vpa.combine_stats(st, stream=side)
+    dst, bst = vpa.verify_stats(x, v, wd, s, r, k, stream=side)
+    out = vpa.greedy_verify(dst, bst, dd, stream=side)
+    side.synchronize()
+    assert torch.equal(ids.cpu(), tgt) and torch.equal(ids2.cpu(), tgt)
+    assert torch.equal(vb.cpu().to(torch.int64) & 0xFFFFFFFF, vals)
+    for a, b in zip(out, oracle.greedy_verify_logits(w.logits, v, drafts)):
+        assert torch.equal(a.cpu(), b)
+
+
 def test_hip_graph_replays_match_eager():
     """The draft argmax and the verification captured in one HIP graph: every
     replay, with new logits copied in and eager work and synchronisation in

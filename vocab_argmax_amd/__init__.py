@@ -116,10 +116,29 @@ def _vp(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream):
+def _stream(stream, device):
+    """The HIP stream to enqueue on: the given torch stream, else the current
+    stream of `device` (the device the call's tensors live on)."""
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(device)
+    elif stream.device != device:
+        raise ValueError(f"stream belongs to {stream.device}, the tensors to {device}")
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _on(device, fn, *args):
+    """Call the library with `device` current (launches go to the current
+    device), switching only when another device is current."""
+    if device.index is not None and torch.cuda.current_device() != device.index:
+        with torch.cuda.device(device):
+            return fn(*args)
+    return fn(*args)
+
+
+def _same_device(device, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
 def _dtype_code(x):
@@ -181,12 +200,12 @@ def block_stats(logits, vocab, shard_width, n_shards, block, rows=None, first_sh
     if out is None:
         out = torch.empty((n_local, n_rows, m, 2), dtype=torch.int32, device=logits.device)
     _stats_tensor(out, "out")
+    _same_device(logits.device, out=out)
     if tuple(out.shape) != (n_local, n_rows, m, 2):
         raise ValueError(f"out has shape {tuple(out.shape)}, expected {(n_local, n_rows, m, 2)}")
-    _check(lib().vpa_block_stats(_vp(logits), _dtype_code(logits), ld,
-                                 Vocab(vocab, shard_width, n_shards), first_shard, n_local,
-                                 _vp(rows), n_rows, logits.shape[0], block, _vp(out),
-                                 _stream(stream)))
+    _check(_on(logits.device, lib().vpa_block_stats, _vp(logits), _dtype_code(logits), ld,
+               Vocab(vocab, shard_width, n_shards), first_shard, n_local, _vp(rows), n_rows,
+               logits.shape[0], block, _vp(out), _stream(stream, logits.device)))
     return out
 
 
@@ -215,9 +234,10 @@ def verify_stats(logits, vocab, shard_width, n_shards, n_req, k, block_draft=DRA
             raise ValueError("preallocated verification statistics have the wrong shape")
     _stats_tensor(dst, "draft_stats")
     _stats_tensor(bst, "bonus_stats")
-    _check(lib().vpa_verify_stats(_vp(logits), _dtype_code(logits), ld,
-                                  Vocab(vocab, shard_width, n_shards), first_shard, n_local, n_req,
-                                  k, block_draft, block_bonus, _vp(dst), _vp(bst), _stream(stream)))
+    _same_device(logits.device, draft_stats=dst, bonus_stats=bst)
+    _check(_on(logits.device, lib().vpa_verify_stats, _vp(logits), _dtype_code(logits), ld,
+               Vocab(vocab, shard_width, n_shards), first_shard, n_local, n_req, k, block_draft,
+               block_bonus, _vp(dst), _vp(bst), _stream(stream, logits.device)))
     return dst, bst
 
 
@@ -247,8 +267,8 @@ def combine_stats(stats, d2t=None, scale=1.0, stream=None):
     vals = torch.empty(n, dtype=torch.int32, device=stats.device)
     mapped = torch.empty(n, dtype=torch.int64, device=stats.device) if d2t is not None else None
     epi, _keep = _epilogue(d2t, scale, stats.device)
-    _check(lib().vpa_combine_stats(_vp(stats), s, n, m, epi, _vp(ids), _vp(vals), _vp(mapped),
-                                   _stream(stream)))
+    _check(_on(stats.device, lib().vpa_combine_stats, _vp(stats), s, n, m, epi, _vp(ids), _vp(vals),
+               _vp(mapped), _stream(stream, stats.device)))
     return (ids, vals) if d2t is None else (ids, vals, mapped)
 
 
@@ -276,12 +296,12 @@ def top_tokens(logits, vocab, shard_width, n_shards, block=DRAFT_BLOCK, workspac
         val_bits = torch.empty(n, dtype=torch.int32, device=logits.device)
     if d2t is not None and mapped is None:
         mapped = torch.empty(n, dtype=torch.int64, device=logits.device)
+    _same_device(logits.device, workspace=workspace, ids=ids, val_bits=val_bits, mapped=mapped)
     epi, _keep = _epilogue(d2t, scale, logits.device)
-    _check(lib().vpa_top_tokens(_vp(logits), _dtype_code(logits), ld,
-                                Vocab(vocab, shard_width, n_shards), n, block, _vp(workspace),
-                                workspace.numel() * workspace.element_size(), epi, _vp(ids),
-                                _vp(val_bits), _vp(mapped if d2t is not None else None),
-                                _stream(stream)))
+    _check(_on(logits.device, lib().vpa_top_tokens, _vp(logits), _dtype_code(logits), ld,
+               Vocab(vocab, shard_width, n_shards), n, block, _vp(workspace),
+               workspace.numel() * workspace.element_size(), epi, _vp(ids), _vp(val_bits),
+               _vp(mapped if d2t is not None else None), _stream(stream, logits.device)))
     return (ids, val_bits) if d2t is None else (ids, val_bits, mapped)
 
 
@@ -312,9 +332,11 @@ def greedy_verify(draft_stats, bonus_stats, draft_ids, with_targets=True, out=No
             if t is not None and (tuple(t.shape) != shape or t.dtype != torch.int32
                                   or not t.is_contiguous()):
                 raise ValueError("preallocated verification outputs have the wrong shape/dtype")
-    _check(lib().vpa_greedy_verify(_vp(draft_stats), draft_stats.shape[2], _vp(bonus_stats),
-                                   bonus_stats.shape[2], s, r, k, _vp(draft_ids), _vp(out_t),
-                                   _vp(ns), _vp(nr), _vp(tg), _stream(stream)))
+        _same_device(dev, out_tokens=out_t, num_sampled=ns, num_rejected=nr, target_ids=tg)
+    _same_device(dev, bonus_stats=bonus_stats)
+    _check(_on(dev, lib().vpa_greedy_verify, _vp(draft_stats), draft_stats.shape[2],
+               _vp(bonus_stats), bonus_stats.shape[2], s, r, k, _vp(draft_ids), _vp(out_t), _vp(ns),
+               _vp(nr), _vp(tg), _stream(stream, dev)))
     return out_t, ns, nr, tg
 
 
@@ -333,8 +355,8 @@ def ragged_rows(cu, total_drafts=None, stream=None):
     n_req = cu.numel() - 1
     draft_rows = torch.empty(total, dtype=torch.int32, device=cu.device)
     bonus_rows = torch.empty(n_req, dtype=torch.int32, device=cu.device)
-    _check(lib().vpa_ragged_rows(_vp(cu), n_req, total, _vp(draft_rows), _vp(bonus_rows),
-                                 _stream(stream)))
+    _check(_on(cu.device, lib().vpa_ragged_rows, _vp(cu), n_req, total, _vp(draft_rows),
+               _vp(bonus_rows), _stream(stream, cu.device)))
     return draft_rows, bonus_rows
 
 
@@ -352,11 +374,10 @@ def verify_stats_rows(logits, vocab, shard_width, n_shards, draft_rows, bonus_ro
     mb = stats_slots(shard_width, n_shards, block_bonus)
     dst = torch.empty((n_local, draft_rows.numel(), md, 2), dtype=torch.int32, device=logits.device)
     bst = torch.empty((n_local, bonus_rows.numel(), mb, 2), dtype=torch.int32, device=logits.device)
-    _check(lib().vpa_verify_stats_rows(_vp(logits), _dtype_code(logits), ld,
-                                       Vocab(vocab, shard_width, n_shards), first_shard, n_local,
-                                       _vp(draft_rows), draft_rows.numel(), _vp(bonus_rows),
-                                       bonus_rows.numel(), logits.shape[0], block_draft,
-                                       block_bonus, _vp(dst), _vp(bst), _stream(stream)))
+    _check(_on(logits.device, lib().vpa_verify_stats_rows, _vp(logits), _dtype_code(logits), ld,
+               Vocab(vocab, shard_width, n_shards), first_shard, n_local, _vp(draft_rows),
+               draft_rows.numel(), _vp(bonus_rows), bonus_rows.numel(), logits.shape[0],
+               block_draft, block_bonus, _vp(dst), _vp(bst), _stream(stream, logits.device)))
     return dst, bst
 
 
@@ -380,10 +401,9 @@ def greedy_verify_ragged(draft_stats, bonus_stats, cu, draft_ids, total_drafts=N
     ns = torch.empty(n_req, dtype=torch.int32, device=dev)
     nr = torch.empty(n_req, dtype=torch.int32, device=dev)
     tg = torch.empty(total + n_req, dtype=torch.int32, device=dev) if with_targets else None
-    _check(lib().vpa_greedy_verify_ragged(_vp(draft_stats), draft_stats.shape[2], _vp(bonus_stats),
-                                          bonus_stats.shape[2], bonus_stats.shape[0], n_req,
-                                          _vp(cu), total, _vp(draft_ids), _vp(out), _vp(ns),
-                                          _vp(nr), _vp(tg), _stream(stream)))
+    _check(_on(dev, lib().vpa_greedy_verify_ragged, _vp(draft_stats), draft_stats.shape[2],
+               _vp(bonus_stats), bonus_stats.shape[2], bonus_stats.shape[0], n_req, _vp(cu), total,
+               _vp(draft_ids), _vp(out), _vp(ns), _vp(nr), _vp(tg), _stream(stream, dev)))
     return out, ns, nr, tg
 
 
