@@ -309,6 +309,34 @@ def test_random_geometries():
         assert_same(vals.to(torch.int64) & 0xFFFFFFFF, want_vals, name + " vals")
 
 
+def test_random_verification_geometries():
+    """Random V, S, W, K, request count, block pair and dtype, with special
+    values in the logits and drafts that copy the target, draw uniformly,
+    or are placeholders: verification statistics and the greedy finish
+    against the oracle (which also checks them against full-row argmax)."""
+    rng = random.Random(777)
+    for trial in range(40):
+        dtype = torch.float32 if trial % 2 else torch.bfloat16
+        s = rng.choice([1, 2, 3, 4, 8])
+        vocab = rng.choice([2, 63, 1000, 4097, 50257])
+        w = -(-vocab // s) + rng.choice([0, 1, 64])
+        k = rng.choice([1, 2, 3, 5, 7, 15])
+        n_req = rng.choice([1, 2, 5, 13])
+        bd, bb = rng.choice([(8192, 1024), (1024, 256), (256, 64), (4096, 8192), (1 << 20, 1)])
+        if vocab > 10000 and min(bd, bb) < 64:
+            bd, bb = 8192, 1024
+        rows = n_req * (k + 1) + rng.choice([0, 3])
+        x = oracle_pins._special_matrix(rows, s * w, 7000 + trial, dtype)
+        x[:, vocab:] = float("nan")
+        tgt, _ = oracle.argmax(x, vocab)
+        g = torch.Generator().manual_seed(7000 + trial)
+        plan = torch.randint(-1, 2, (n_req, k), generator=g).to(torch.int8)
+        uni = torch.randint(0, vocab, (n_req, k), generator=g, dtype=torch.int64).to(torch.int32)
+        drafts = workloads.compose_drafts(tgt[:n_req * (k + 1)].reshape(n_req, k + 1), plan, uni)
+        _verify_both(x, vocab, w, s, n_req, k, drafts, bd, bb,
+                     f"random verify {trial} V={vocab} S={s} W={w} K={k} R={n_req} B={bd}/{bb} {dtype}")
+
+
 def test_long_segments_and_chunk_cascade():
     """Blocks far larger than one pipelined chunk (many chunks per segment),
     segments that end part-way through a chunk, and ties planted far
