@@ -219,6 +219,27 @@ def test_ragged_verify(seed, vocab, s, n_req, kmax):
         assert_same(g, wv, "verify_ragged")
 
 
+def test_random_ragged_batches():
+    """30 random ragged batches (draft counts 0..K_max per request, both
+    dtypes, several vocabularies and shard counts): the whole ragged path
+    against the oracle's ragged verification from full logits."""
+    rng = random.Random(31)
+    for trial in range(30):
+        vocab = rng.choice([5, 1000, 4097, 50257])
+        s = rng.choice([1, 2, 3, 8])
+        n_req = rng.choice([1, 3, 17, 64])
+        kmax = rng.choice([0, 1, 4, 9])
+        dtype = torch.float32 if trial % 3 == 0 else torch.bfloat16
+        x_cpu, v, w, s, cu, drafts = _ragged_case(100 + trial, vocab, s, n_req, kmax, dtype,
+                                                  p_copy=rng.random())
+        total = int(cu[-1])
+        _announce(f"random ragged {trial} V={v} S={s} R={n_req} Kmax={kmax} total={total} {dtype}")
+        want = oracle.greedy_verify_ragged(x_cpu, v, cu, drafts)
+        got = vpa.verify_ragged(_dev(x_cpu), v, w, s, _dev(cu), _dev(drafts), total)
+        for a, b, nm in zip(got, want, ("out_tokens", "num_sampled", "num_rejected", "target_ids")):
+            assert_same(a, b, f"random ragged {trial} {nm}")
+
+
 def test_ragged_malformed_offsets_are_flagged():
     """Offsets that decrease or run past the total: that request reports -1
     counts and writes no tokens; the others are unaffected."""
