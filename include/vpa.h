@@ -50,8 +50,10 @@
  *    pattern h widens to h<<16), NaN payload and the sign of zero kept.
  *  - Results are deterministic: the same inputs give bitwise identical
  *    outputs on every run, whatever the launch shape.
- *  - The library is greedy-only: it assumes the caller has already applied
- *    any positive logit scale and routes sampled requests elsewhere.
+ *  - The library is greedy-only: the argmax is taken over the logits as
+ *    given (a logit scale, which must be positive to keep the argmax, is
+ *    the caller's; the optional epilogue scale below only rescales the
+ *    reported maxima), and sampled requests are routed elsewhere.
  */
 #ifndef VPA_H
 #define VPA_H
@@ -89,7 +91,7 @@ typedef struct {
 /* Vocabulary geometry: V valid columns, S shards of W columns each. */
 typedef struct {
     int64_t vocab;       /* V, 1 <= V < 2^24 */
-    int64_t shard_width; /* W >= 1 */
+    int64_t shard_width; /* 1 <= W < 2^31 */
     int32_t n_shards;    /* 1 <= S <= VPA_MAX_SHARDS, S*W >= V (a shard may hold only padding) */
 } vpa_vocab;
 
@@ -129,7 +131,8 @@ int32_t vpa_stats_slots(int64_t shard_width, int32_t n_shards, int32_t block);
  *  rows     n_rows int32 row indices into logits, or NULL for 0..n_rows-1.
  *           An index outside [0, logits_rows) yields empty statistics for
  *           that row and reads nothing.
- *  logits_rows  number of rows the logits buffer holds (bounds rows[]).
+ *  logits_rows  number of rows the logits buffer holds: it bounds rows[],
+ *           and with rows NULL it must be at least n_rows.
  *  block    global block size (>= 1).
  *  stats    out, [n_local_shards][n_rows][M] with M = vpa_stats_slots(W,S,block),
  *           8-byte aligned.  Slot i of shard s describes row rows[i]. */
