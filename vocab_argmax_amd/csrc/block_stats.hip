@@ -56,15 +56,21 @@ constexpr int kWaves = VPA_WAVES_PER_WG;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kLaneIters = VPA_LANE_ITERS;   // target iterations per lane of a segment
 
-// LDS reserved per workgroup at launch and never touched by the kernel.
-// 32 KiB lets LDS alone hold a CU to 5 workgroups (20 wavefronts); on
-// MI355X the statistics launches measured 2-3 % faster with it than with
-// no or smaller reservations, which leave the same 5 workgroups per CU to
-// the register limit.
+// LDS reserved per workgroup at launch and never touched by the kernel, by
+// element size.  bf16: 32 KiB lets LDS alone hold a CU to 5 workgroups
+// (20 wavefronts), the count the registers allow too; on MI355X the
+// statistics launches measured 2-3 % faster with it than with no or smaller
+// reservations.  fp32 (150 VGPRs, 3 workgroups per CU by registers): 64 KiB,
+// 2 workgroups per CU, measured 2-3 % faster than 32 or 48 KiB.
 #ifndef VPA_LDS_RESERVE_KB
 #define VPA_LDS_RESERVE_KB 32
 #endif
-constexpr unsigned kLdsReserve = VPA_LDS_RESERVE_KB * 1024u;
+#ifndef VPA_LDS_RESERVE_F32_KB
+#define VPA_LDS_RESERVE_F32_KB 64
+#endif
+template <int ESIZE>
+constexpr unsigned kLdsReserve =
+    (ESIZE == 2 ? VPA_LDS_RESERVE_KB : VPA_LDS_RESERVE_F32_KB) * 1024u;
 
 // Group iterations per pipelined chunk, by element size.
 template <int ESIZE>
@@ -350,9 +356,9 @@ hipError_t launch_block_stats(int esize, const SegTask& t0_in, const SegTask& t1
     const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves));
     const dim3 block(kThreads);
     if (esize == 2)
-        hipLaunchKernelGGL(block_stats_kernel<2>, grid, block, kLdsReserve, stream, t0, t1);
+        hipLaunchKernelGGL(block_stats_kernel<2>, grid, block, kLdsReserve<2>, stream, t0, t1);
     else
-        hipLaunchKernelGGL(block_stats_kernel<4>, grid, block, kLdsReserve, stream, t0, t1);
+        hipLaunchKernelGGL(block_stats_kernel<4>, grid, block, kLdsReserve<4>, stream, t0, t1);
     return hipGetLastError();
 }
 
