@@ -14,7 +14,8 @@
 // workgroup, no LDS and no barriers.  The loads come in chunks of U group
 // iterations, software-pipelined: chunk c+1 is issued before chunk c is
 // folded, so a wavefront keeps U to 2U loads in flight.  U = 8 for bf16
-// (91 VGPRs, 5 wavefronts per SIMD) and 16 for fp32 measured fastest on
+// (91 VGPRs, 5 wavefronts per SIMD) and 16 for fp32 (150 VGPRs, held to 2
+// wavefronts per SIMD by the launch's LDS reservation) measured fastest on
 // MI355X.  Each lane keeps a running best, and a shuffle reduction inside
 // the group finishes the segment.  Consecutive groups and wavefronts take
 // consecutive segments of a row, so a wavefront reads contiguous memory.
