@@ -2,6 +2,7 @@
 verification outputs) must equal the CPU oracle's bit for bit, on the same
 seeded inputs.  The inputs are generated on the CPU (workloads.py), copied to
 the device for the HIP path, and handed unchanged to the oracle."""
+import ctypes
 import random
 
 import pytest
@@ -600,6 +601,33 @@ def test_explicit_stream_argument():
     assert torch.equal(vb.cpu().to(torch.int64) & 0xFFFFFFFF, vals)
     for a, b in zip(out, oracle.greedy_verify_logits(w.logits, v, drafts)):
         assert torch.equal(a.cpu(), b)
+
+
+def test_stale_runtime_error_is_left_to_its_owner():
+    """A failed, unrelated HIP runtime call earlier in the process (here an
+    invalid device number, a host-side argument error) neither fails the
+    library's next call nor is consumed by it."""
+    w = workloads.config2()
+    v, wd, s = w.vocab, w.shard_width, w.n_shards
+    x = _dev(w.logits)
+    n = x.shape[0]
+    ws = torch.empty(vpa.top_tokens_workspace(v, wd, s, n, 8192), dtype=torch.uint8, device=DEV)
+    ids = torch.empty(n, dtype=torch.int32, device=DEV)
+    vals = torch.empty(n, dtype=torch.int32, device=DEV)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    hip = ctypes.CDLL("libamdhip64.so")
+    assert hip.hipSetDevice(999) != 0
+    status = vpa.lib().vpa_top_tokens(ctypes.c_void_p(x.data_ptr()), vpa.VPA_BF16, x.stride(0),
+                                      vpa.Vocab(v, wd, s), n, 8192, ctypes.c_void_p(ws.data_ptr()),
+                                      ws.numel(), None, ctypes.c_void_p(ids.data_ptr()),
+                                      ctypes.c_void_p(vals.data_ptr()), None, stream)
+    stale = hip.hipGetLastError()
+    assert status == vpa.VPA_OK, vpa.last_error()
+    assert stale != 0                     # still there for the code that caused it
+    want_ids, want_vals = oracle.argmax(w.logits, v)
+    assert_same(ids, want_ids, "ids after a stale error")
+    assert_same(vals.to(torch.int64) & 0xFFFFFFFF, want_vals, "vals after a stale error")
 
 
 def test_hip_graph_replays_match_eager():

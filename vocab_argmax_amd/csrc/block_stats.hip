@@ -356,11 +356,8 @@ hipError_t launch_block_stats(int esize, const SegTask& t0_in, const SegTask& t1
         return hipSuccess;
     const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves));
     const dim3 block(kThreads);
-    if (esize == 2)
-        hipLaunchKernelGGL(block_stats_kernel<2>, grid, block, kLdsReserve<2>, stream, t0, t1);
-    else
-        hipLaunchKernelGGL(block_stats_kernel<4>, grid, block, kLdsReserve<4>, stream, t0, t1);
-    return hipGetLastError();
+    return esize == 2 ? launch(block_stats_kernel<2>, grid, block, kLdsReserve<2>, stream, t0, t1)
+                      : launch(block_stats_kernel<4>, grid, block, kLdsReserve<4>, stream, t0, t1);
 }
 
 }  // namespace vpa

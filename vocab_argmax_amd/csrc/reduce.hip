@@ -214,9 +214,8 @@ int64_t greedy_verify_ragged_threads(int32_t n_req) {
 hipError_t launch_ragged_rows(const int32_t* cu, int32_t n_req, int32_t total_drafts,
                               int32_t* draft_rows, int32_t* bonus_rows, hipStream_t stream) {
     const dim3 grid((unsigned)((n_req + kThreads - 1) / kThreads));
-    hipLaunchKernelGGL(ragged_rows_kernel, grid, dim3(kThreads), 0, stream, cu, n_req,
-                       total_drafts, draft_rows, bonus_rows);
-    return hipGetLastError();
+    return launch(ragged_rows_kernel, grid, dim3(kThreads), 0, stream, cu, n_req, total_drafts,
+                  draft_rows, bonus_rows);
 }
 
 hipError_t launch_greedy_verify_ragged(const vpa_stat* draft_stats, int32_t m_draft,
@@ -226,20 +225,17 @@ hipError_t launch_greedy_verify_ragged(const vpa_stat* draft_stats, int32_t m_dr
                                        int32_t* out_tokens, int32_t* num_sampled,
                                        int32_t* num_rejected, int32_t* target_ids,
                                        hipStream_t stream) {
-    hipLaunchKernelGGL(greedy_verify_ragged_kernel, dim3((unsigned)n_req), dim3(kThreads), 0,
-                       stream, draft_stats, m_draft, bonus_stats, m_bonus, n_shards, n_req, cu,
-                       total_drafts, draft_ids, out_tokens, num_sampled, num_rejected,
-                       target_ids);
-    return hipGetLastError();
+    return launch(greedy_verify_ragged_kernel, dim3((unsigned)n_req), dim3(kThreads), 0, stream,
+                  draft_stats, m_draft, bonus_stats, m_bonus, n_shards, n_req, cu, total_drafts,
+                  draft_ids, out_tokens, num_sampled, num_rejected, target_ids);
 }
 
 hipError_t launch_combine(const vpa_stat* stats, int32_t n_shards, int32_t n_rows, int32_t m,
                           const int64_t* d2t, int64_t d2t_len, float scale, int32_t* ids,
                           uint32_t* val_bits, int64_t* mapped, hipStream_t stream) {
     const dim3 grid((unsigned)((n_rows + kWaves - 1) / kWaves));
-    hipLaunchKernelGGL(combine_kernel, grid, dim3(kThreads), 0, stream, stats, n_shards, n_rows, m,
-                       d2t, d2t_len, scale, ids, val_bits, mapped);
-    return hipGetLastError();
+    return launch(combine_kernel, grid, dim3(kThreads), 0, stream, stats, n_shards, n_rows, m, d2t,
+                  d2t_len, scale, ids, val_bits, mapped);
 }
 
 hipError_t launch_greedy_verify(const vpa_stat* draft_stats, int32_t m_draft,
@@ -248,11 +244,10 @@ hipError_t launch_greedy_verify(const vpa_stat* draft_stats, int32_t m_draft,
                                 int32_t* out_tokens, int32_t* num_sampled, int32_t* num_rejected,
                                 int32_t* target_ids, hipStream_t stream) {
     const int32_t waves = k + 1 < kVerifyMaxThreads / 64 ? k + 1 : kVerifyMaxThreads / 64;
-    hipLaunchKernelGGL(greedy_verify_kernel, dim3((unsigned)n_req), dim3(64 * waves),
-                       (size_t)(k + 1) * sizeof(int32_t), stream, draft_stats, m_draft,
-                       bonus_stats, m_bonus, n_shards, n_req, k, draft_ids, out_tokens,
-                       num_sampled, num_rejected, target_ids);
-    return hipGetLastError();
+    return launch(greedy_verify_kernel, dim3((unsigned)n_req), dim3(64 * waves),
+                  (size_t)(k + 1) * sizeof(int32_t), stream, draft_stats, m_draft, bonus_stats,
+                  m_bonus, n_shards, n_req, k, draft_ids, out_tokens, num_sampled, num_rejected,
+                  target_ids);
 }
 
 }  // namespace vpa

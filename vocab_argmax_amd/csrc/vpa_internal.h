@@ -9,6 +9,22 @@
 
 namespace vpa {
 
+template <typename T>
+struct same_type {
+    using type = T;
+};
+
+// Launch `kernel` and return the status of this launch alone: not an error
+// left behind by an earlier, unrelated HIP call, which stays where the
+// caller can see it.  Arguments convert to the kernel's parameter types.
+template <typename... Params>
+hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, size_t lds_bytes,
+                  hipStream_t stream, typename same_type<Params>::type... args) {
+    void* ptrs[] = {(void*)&args..., nullptr};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, lds_bytes,
+                           stream);
+}
+
 // One launch's worth of (row, shard, slot) work items for the block-statistics
 // kernel.  Item t decodes as row i = t / (n_local*m), local shard
 // sl = (t / m) % n_local, slot j = t % m; consecutive items therefore walk a
