@@ -30,8 +30,7 @@
  *       order, as a dim-0 all-gather lays them out; placeholder drafts;
  *       unaligned padding; NaN rows stay inside the vocabulary.
  *
- * Readings where the pages leave a step open (each is listed with its
- * justification in the design notes of the repository):
+ * Readings where the pages leave a step open:
  *  - among several NaNs the lowest id wins (first occurrence, as
  *    torch.argmax);
  *  - -0 and +0 compare equal, so the lower id wins;
