@@ -24,8 +24,9 @@ of vpa_verify_stats, whose average duration HIP events on the launch stream
 measure over back-to-back launches right after the timed steps (median of 5
 windows), against MI355X's 8 TB/s HBM peak; top_tokens_rows_sweep = the fused
 argmax alone at 1024, 2048 and 4096 bf16 rows and 1024 fp32 rows, alternating
-two input buffers; cpu_baseline = the CPU oracle timed on this host on the
-same step.
+two input buffers; small_configs_us = the 32-row argmax and the 24 x 4-row
+verification from Python and replayed from HIP graphs; cpu_baseline = the CPU
+oracle timed on this host on the same step.
 """
 import argparse
 import hashlib
@@ -349,6 +350,17 @@ def main():
         vpa.top_tokens(x2, w2.vocab, w2.shard_width, w2.n_shards, 8192, workspace=ws2)
         verify3()
     small["graph_top_tokens_32_plus_verify_24x4"] = per_call(g_small.replay) * 1e6
+    # each alone, replayed from a graph of 20 back-to-back copies: the GPU
+    # time of one decode-sized call
+    for name, fn in (("graph_top_tokens_32x151936_s2",
+                      lambda: vpa.top_tokens(x2, w2.vocab, w2.shard_width, w2.n_shards, 8192,
+                                             workspace=ws2)),
+                     ("graph_verify_24x4_rows_200064_s4", verify3)):
+        g_one = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_one):
+            for _ in range(20):
+                fn()
+        small[name] = per_call(g_one.replay) / 20 * 1e6
     result["small_configs_us"] = small
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
