@@ -25,8 +25,11 @@ measure over back-to-back launches right after the timed steps (median of 5
 windows), against MI355X's 8 TB/s HBM peak; top_tokens_rows_sweep = the fused
 argmax alone at 1024, 2048 and 4096 bf16 rows and 1024 fp32 rows, alternating
 two input buffers; small_configs_us = the 32-row argmax and the 24 x 4-row
-verification from Python and replayed from HIP graphs; cpu_baseline = the CPU
-oracle timed on this host on the same step.
+verification from Python and replayed from HIP graphs; read_ceiling = a plain
+persistent read of the same two 1.64 GB buffers (libvpa_probe.so), the
+practical HBM read rate of this GPU, beside which the roofline's achieved
+rate is set; cpu_baseline = the CPU oracle timed on this host on the same
+step.
 """
 import argparse
 import hashlib
@@ -274,6 +277,20 @@ def main():
     sweep[f"fp32_n{F32_ROWS}"] = rows_sweep(f32_bufs, F32_ROWS, 4)
     del f32_bufs
 
+    # the practical read ceiling: a read-only persistent kernel over the same
+    # two buffers, alternating, timed like the calls above
+    from vocab_argmax_amd import read_probe
+    n_wg = read_probe.default_workgroups(dev)
+    sink = read_probe.make_sink(dev, n_wg)
+    probe_bufs = (xd, xt)
+    probe_flip = [0]
+    probe_bytes = [0]
+
+    def probe_call():
+        probe_bytes[0] = read_probe.read(probe_bufs[probe_flip[0]], sink, n_wg)
+        probe_flip[0] ^= 1
+    probe_s = per_call(probe_call, 2 * n_k)
+
     ms_step = max(wall, gpu) * 1e3 / args.steps
     alg = algorithmic_bytes()
     step_bytes = sum(alg.values())
@@ -318,6 +335,16 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": alg["verify_stats"],
             "avg_launch_us": vs_s * 1e6,
+        },
+        "read_ceiling": {
+            "probe": (f"read-only persistent grid ({n_wg} workgroups of 256 threads, "
+                      f"{read_probe.WORKGROUPS_PER_CU} per CU), 16-byte non-temporal loads in "
+                      "4 KiB chunks, one chunk ahead"),
+            "bytes_per_launch": probe_bytes[0],
+            "avg_launch_us": probe_s * 1e6,
+            "gbps": probe_bytes[0] / probe_s / 1e9,
+            "frac_of_peak": probe_bytes[0] / probe_s / 1e9 / PEAK_HBM_GBPS,
+            "roofline_achieved_over_ceiling": achieved / (probe_bytes[0] / probe_s / 1e9),
         },
         "cpu_baseline": None,
     }

@@ -5,6 +5,9 @@
 Sources are compiled in parallel into vocab_argmax_amd/_build/ and linked into
 vocab_argmax_amd/libvpa.so.  Packed-fp32 instructions are disabled for the
 device code (the path has no float arithmetic; the flag keeps it that way).
+The HBM read-ceiling probe (csrc/read_probe.hip, include/vpa_probe.h) is
+built on its own into vocab_argmax_amd/libvpa_probe.so: only the benchmark
+and its test load it.
 """
 import os
 import shutil
@@ -18,6 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libvpa.so")
 SOURCES = ["api.hip", "block_stats.hip", "reduce.hip"]
+PROBE_LIB = os.path.join(PKG, "libvpa_probe.so")
+PROBE_SOURCES = ["read_probe.hip"]
 ARCH = "gfx950"
 
 
@@ -50,15 +55,19 @@ def build(verbose: bool = False, extra_flags=()) -> str:
             raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}\n{res.stderr}")
         return obj
 
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(one, SOURCES))
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(LIB + ".tmp", LIB)
+    def link(objs, out):
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out + ".tmp"]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
+        os.replace(out + ".tmp", out)
+
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + len(PROBE_SOURCES)) as ex:
+        objs = list(ex.map(one, SOURCES + PROBE_SOURCES))
+    link(objs[:len(SOURCES)], LIB)
+    link(objs[len(SOURCES):], PROBE_LIB)
     return LIB
 
 
