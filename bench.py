@@ -88,7 +88,7 @@ def measured_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(draft_cpu, target_cpu, drafts_cpu, gpu_out, min_seconds=10.0, max_reps=5):
+def cpu_baseline(draft_cpu, target_cpu, drafts_cpu, gpu_out, min_seconds=10.0, max_reps=10):
     """The CPU oracle on the same step, single-threaded, pinned to one core."""
     import oracle
     import torch
