@@ -44,10 +44,10 @@ def _bind(lib):
                                                  vp, vp, vp]
     lib.vpa_ref_greedy_verify_logits.restype = None
     lib.vpa_ref_greedy_verify_ragged.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, vp,
-                                                 vp, vp]
+                                                 vp, vp, vp]
     lib.vpa_ref_greedy_verify_ragged.restype = None
     lib.vpa_ref_greedy_verify_ragged_stats.argtypes = [vp, i32, vp, i32, i32, i64, vp, vp, vp, vp,
-                                                       vp, vp]
+                                                       vp, vp, vp]
     lib.vpa_ref_greedy_verify_ragged_stats.restype = None
     lib.vpa_ref_map_ids.argtypes = [vp, i64, vp, i64, vp]
     lib.vpa_ref_map_ids.restype = None
@@ -74,6 +74,16 @@ def _check_logits(x: torch.Tensor) -> int:
 
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else None
+
+
+def _flags(flags, n):
+    """Optional per-request flags as a contiguous uint8 [n] tensor (None stays None)."""
+    if flags is None:
+        return None
+    flags = torch.as_tensor(flags).to("cpu").ne(0).to(torch.uint8).contiguous()
+    if flags.numel() != n:
+        raise ValueError(f"{flags.numel()} flags for {n} requests")
+    return flags
 
 
 class Oracle:
@@ -161,14 +171,16 @@ class Oracle:
 
 
     def greedy_verify_ragged(self, x: torch.Tensor, vocab: int, cu: torch.Tensor,
-                             draft_ids: torch.Tensor):
+                             draft_ids: torch.Tensor, prefilling=None):
         """Ragged greedy verification from full logits.  cu int32 [R+1] cumulative
-        draft counts; request r owns rows cu[r]+r..cu[r]+r+K_r.  Returns
+        draft counts; request r owns rows cu[r]+r..cu[r]+r+K_r; prefilling: optional
+        [R] flags (nonzero = still prefilling: samples nothing).  Returns
         (out_tokens [cu[R]+R], num_sampled [R], num_rejected [R], target_ids [cu[R]+R])."""
         ld = _check_logits(x)
         cu = cu.to(torch.int32).contiguous()
         draft_ids = draft_ids.to(torch.int32).contiguous()
         r = cu.numel() - 1
+        pf = _flags(prefilling, r)
         total = int(cu[-1]) if r > 0 else 0
         if x.shape[0] < total + r:
             raise ValueError("logits have fewer rows than drafts + requests")
@@ -178,18 +190,19 @@ class Oracle:
         tg = torch.empty(total + r, dtype=torch.int32)
         if r:
             self.lib.vpa_ref_greedy_verify_ragged(_ptr(x), _dtype_code(x), ld, vocab, r, _ptr(cu),
-                                                  _ptr(draft_ids), _ptr(out), _ptr(ns), _ptr(nr),
-                                                  _ptr(tg))
+                                                  _ptr(draft_ids), _ptr(pf), _ptr(out), _ptr(ns),
+                                                  _ptr(nr), _ptr(tg))
         return out, ns, nr, tg
 
     def greedy_verify_ragged_stats(self, draft_stats: torch.Tensor, bonus_stats: torch.Tensor,
-                                   cu: torch.Tensor, draft_ids: torch.Tensor):
+                                   cu: torch.Tensor, draft_ids: torch.Tensor, prefilling=None):
         """Ragged greedy verification from statistics [S][cu[R]][Md][2], [S][R][Mb][2]."""
         draft_stats = draft_stats.contiguous()
         bonus_stats = bonus_stats.contiguous()
         cu = cu.to(torch.int32).contiguous()
         draft_ids = draft_ids.to(torch.int32).contiguous()
         r = cu.numel() - 1
+        pf = _flags(prefilling, r)
         total = int(cu[-1]) if r > 0 else 0
         s, md, mb = draft_stats.shape[0], draft_stats.shape[2], bonus_stats.shape[2]
         out = torch.empty(total + r, dtype=torch.int32)
@@ -199,7 +212,8 @@ class Oracle:
         if r:
             self.lib.vpa_ref_greedy_verify_ragged_stats(_ptr(draft_stats), md, _ptr(bonus_stats),
                                                         mb, s, r, _ptr(cu), _ptr(draft_ids),
-                                                        _ptr(out), _ptr(ns), _ptr(nr), _ptr(tg))
+                                                        _ptr(pf), _ptr(out), _ptr(ns), _ptr(nr),
+                                                        _ptr(tg))
         return out, ns, nr, tg
 
     def map_ids(self, ids: torch.Tensor, d2t: torch.Tensor):

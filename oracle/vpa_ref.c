@@ -52,6 +52,11 @@
  *    logits rows are cu[r]+r .. cu[r]+r+K_r (drafts, then the bonus
  *    position) and its K_r+1 outputs sit at the same offsets; the greedy
  *    rule is the uniform one with K = K_r (K_r = 0 emits the bonus token).
+ *  - prefilling requests ([P4] "Test Plan" lists them among the verified
+ *    cases but states no rule; the reading taken here): a request flagged as
+ *    still prefilling samples nothing, so all K_r+1 of its output slots
+ *    hold -1 and sampled = rejected = 0; its target tokens are still
+ *    reported.
  *  - optional epilogue of the combined argmax k:
  *    [P2] PR #39419 "[SpecDecode] Reduce TP communication for large-vocab
  *    draft models speculative decoding", note "Refactor local argmax code":
@@ -237,6 +242,16 @@ static void ref_accept(const int32_t *draft, const int32_t *target, int32_t k, i
     *n_rejected = k - n;
 }
 
+/* A request still prefilling samples nothing: K+1 slots of -1, no sampled
+ * and no rejected token. */
+static void ref_prefilling(int32_t k, int32_t *out, int32_t *n_sampled, int32_t *n_rejected)
+{
+    for (int32_t j = 0; j <= k; ++j)
+        out[j] = -1;
+    *n_sampled = 0;
+    *n_rejected = 0;
+}
+
 /* Greedy verification from gathered statistics: draft stats
  * [S][R*K][m_draft] (row i = request i/K, position i%K) and bonus stats
  * [S][R][m_bonus].  target_ids may be NULL. */
@@ -306,9 +321,11 @@ uint32_t vpa_ref_scale_bits(uint32_t bits, float scale)
 /* Ragged greedy verification from full logits: request r owns rows
  * cu[r]+r .. cu[r]+r+K_r (K_r = cu[r+1]-cu[r] drafts, then the bonus row);
  * draft_ids holds the cu[R] drafts back to back; out_tokens and target_ids
- * hold K_r+1 entries per request at offset cu[r]+r. */
+ * hold K_r+1 entries per request at offset cu[r]+r.  prefilling (NULL = none)
+ * flags the requests that are still prefilling. */
 void vpa_ref_greedy_verify_ragged(const void *x, int dtype, int64_t ld, int64_t vocab, int64_t n_req,
-                                  const int32_t *cu, const int32_t *draft_ids, int32_t *out_tokens,
+                                  const int32_t *cu, const int32_t *draft_ids,
+                                  const uint8_t *prefilling, int32_t *out_tokens,
                                   int32_t *num_sampled, int32_t *num_rejected, int32_t *target_ids)
 {
     for (int64_t r = 0; r < n_req; ++r) {
@@ -320,7 +337,11 @@ void vpa_ref_greedy_verify_ragged(const void *x, int dtype, int64_t ld, int64_t 
             const char *row = (const char *)x + (dtype == REF_BF16 ? 2 : 4) * (base + j) * ld;
             vpa_ref_argmax(row, dtype, ld, 1, vocab, &tgt[j], &vb);
         }
-        ref_accept(draft_ids + cu[r], tgt, k, out_tokens + base, num_sampled + r, num_rejected + r);
+        if (prefilling && prefilling[r])
+            ref_prefilling(k, out_tokens + base, num_sampled + r, num_rejected + r);
+        else
+            ref_accept(draft_ids + cu[r], tgt, k, out_tokens + base, num_sampled + r,
+                       num_rejected + r);
         if (target_ids)
             for (int32_t j = 0; j <= k; ++j)
                 target_ids[base + j] = tgt[j];
@@ -333,9 +354,9 @@ void vpa_ref_greedy_verify_ragged(const void *x, int dtype, int64_t ld, int64_t 
 void vpa_ref_greedy_verify_ragged_stats(const ref_stat *draft_stats, int32_t m_draft,
                                         const ref_stat *bonus_stats, int32_t m_bonus,
                                         int32_t n_shards, int64_t n_req, const int32_t *cu,
-                                        const int32_t *draft_ids, int32_t *out_tokens,
-                                        int32_t *num_sampled, int32_t *num_rejected,
-                                        int32_t *target_ids)
+                                        const int32_t *draft_ids, const uint8_t *prefilling,
+                                        int32_t *out_tokens, int32_t *num_sampled,
+                                        int32_t *num_rejected, int32_t *target_ids)
 {
     int64_t total = cu[n_req];
     for (int64_t r = 0; r < n_req; ++r) {
@@ -345,7 +366,11 @@ void vpa_ref_greedy_verify_ragged_stats(const ref_stat *draft_stats, int32_t m_d
         for (int32_t j = 0; j < k; ++j)
             tgt[j] = ref_combine_row(draft_stats, n_shards, total, (int64_t)cu[r] + j, m_draft).id;
         tgt[k] = ref_combine_row(bonus_stats, n_shards, n_req, r, m_bonus).id;
-        ref_accept(draft_ids + cu[r], tgt, k, out_tokens + base, num_sampled + r, num_rejected + r);
+        if (prefilling && prefilling[r])
+            ref_prefilling(k, out_tokens + base, num_sampled + r, num_rejected + r);
+        else
+            ref_accept(draft_ids + cu[r], tgt, k, out_tokens + base, num_sampled + r,
+                       num_rejected + r);
         if (target_ids)
             for (int32_t j = 0; j <= k; ++j)
                 target_ids[base + j] = tgt[j];

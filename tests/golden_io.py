@@ -76,9 +76,13 @@ def epilogue_cases():
 
 
 def ragged_verify_cases():
-    """[(cu, targets, drafts, out_tokens, sampled, rejected)] as int lists."""
+    """[(cu, targets, drafts, out_tokens, sampled, rejected, prefilling)] as int
+    lists; prefilling is None where a case gives no flags."""
     out = []
     for line in _lines("ragged_verify_cases.txt"):
         fields = [[int(t) for t in p.split()] for p in line.split("|")]
+        if len(fields) == 6:
+            fields.append(None)
+        assert len(fields) == 7, line
         out.append(tuple(fields))
     return out

@@ -250,16 +250,18 @@ def _ragged_logits(targets, vocab):
 
 
 def pin_ragged_verify(o):
-    """Ragged verification: hand-worked cases; every request equals the
-    brute-force greedy rule with its own K; statistics and logits agree."""
+    """Ragged verification: hand-worked cases (some with requests still
+    prefilling); every request equals the brute-force greedy rule with its own
+    K, or samples nothing when flagged as prefilling; flagging requests leaves
+    every other request's outputs as they were; statistics and logits agree."""
     import oracle as _oracle
-    for cu, targets, drafts, out, ns, nr in golden_io.ragged_verify_cases():
+    for cu, targets, drafts, out, ns, nr, pf in golden_io.ragged_verify_cases():
         x = _ragged_logits(targets, 16)
         cu_t = torch.tensor(cu, dtype=torch.int32)
         d = torch.tensor(drafts, dtype=torch.int32)
-        got = o.greedy_verify_ragged(x, 16, cu_t, d)
+        got = o.greedy_verify_ragged(x, 16, cu_t, d, prefilling=pf)
         assert got[0].tolist() == out and got[1].tolist() == ns and got[2].tolist() == nr, \
-            (cu, got)
+            (cu, pf, got)
         assert got[3].tolist() == targets
     rng = random.Random(5)
     for trial in range(200):
@@ -271,21 +273,31 @@ def pin_ragged_verify(o):
             cu.append(cu[-1] + k)
         targets = [rng.randrange(vocab) for _ in range(cu[-1] + n_req)]
         drafts = [rng.randint(-1, vocab - 1) for _ in range(cu[-1])]
+        pf = [int(rng.random() < 0.3) for _ in range(n_req)] if trial % 2 else None
         x = _ragged_logits(targets, vocab)
         cu_t = torch.tensor(cu, dtype=torch.int32)
         d = torch.tensor(drafts, dtype=torch.int32)
-        out, ns, nr, tg = o.greedy_verify_ragged(x, vocab, cu_t, d)
+        out, ns, nr, tg = o.greedy_verify_ragged(x, vocab, cu_t, d, prefilling=pf)
         draft_rows, bonus_rows = _oracle.ragged_rows(cu_t)
         dst = o.block_stats(x, vocab, vocab, 1, 1, rows=draft_rows)
         bst = o.block_stats(x, vocab, vocab, 1, 1, rows=bonus_rows)
-        got2 = o.greedy_verify_ragged_stats(dst, bst, cu_t, d)
+        got2 = o.greedy_verify_ragged_stats(dst, bst, cu_t, d, prefilling=pf)
         for a, b in zip((out, ns, nr, tg), got2):
-            assert torch.equal(a, b), (cu, drafts)
+            assert torch.equal(a, b), (cu, drafts, pf)
+        assert tg.tolist() == targets
+        plain = o.greedy_verify_ragged(x, vocab, cu_t, d) if pf else None
         for r, k in enumerate(ks):
             base = cu[r] + r
-            want = bf.bf_verify(targets[base:base + k + 1], drafts[cu[r]:cu[r] + k])
             got = (out[base:base + k + 1].tolist(), int(ns[r]), int(nr[r]))
+            if pf and pf[r]:
+                assert got == ([-1] * (k + 1), 0, 0), (cu, r, got)
+                continue
+            want = bf.bf_verify(targets[base:base + k + 1], drafts[cu[r]:cu[r] + k])
             assert got == want, (cu, r, got, want)
+            if plain is not None:
+                # a flag on other requests changes nothing here
+                assert got == (plain[0][base:base + k + 1].tolist(), int(plain[1][r]),
+                               int(plain[2][r])), (cu, r, pf)
 
 
 ALL_PINS = [pin_golden_argmax, pin_golden_block_stats, pin_golden_verify, pin_exhaustive_argmax,

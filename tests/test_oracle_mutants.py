@@ -54,8 +54,18 @@ MUTANTS = [
      "        int64_t base = (int64_t)cu[r] + r;\n        int32_t tgt[k + 1];\n        uint32_t vb;",
      "        int64_t base = (int64_t)cu[r];\n        int32_t tgt[k + 1];\n        uint32_t vb;"),
     ("ragged_stats_bonus_from_draft_rows",
-     "        tgt[k] = ref_combine_row(bonus_stats, n_shards, n_req, r, m_bonus).id;\n        ref_accept(draft_ids + cu[r]",
-     "        tgt[k] = k ? tgt[k - 1] : 0;\n        ref_accept(draft_ids + cu[r]"),
+     "        tgt[k] = ref_combine_row(bonus_stats, n_shards, n_req, r, m_bonus).id;\n        if (prefilling",
+     "        tgt[k] = k ? tgt[k - 1] : 0;\n        if (prefilling"),
+    ("prefilling_flag_ignored",
+     "            vpa_ref_argmax(row, dtype, ld, 1, vocab, &tgt[j], &vb);\n        }\n        if (prefilling && prefilling[r])",
+     "            vpa_ref_argmax(row, dtype, ld, 1, vocab, &tgt[j], &vb);\n        }\n        if (0)"),
+    ("prefilling_samples_its_bonus",
+     "        out[j] = -1;\n    *n_sampled = 0;", "        out[j] = j == k ? 0 : -1;\n    *n_sampled = 1;"),
+    ("prefilling_rejects_its_drafts",
+     "    *n_sampled = 0;\n    *n_rejected = 0;", "    *n_sampled = 0;\n    *n_rejected = k;"),
+    ("prefilling_flag_of_next_request",
+     "        if (prefilling && prefilling[r])\n            ref_prefilling(k, out_tokens + base, num_sampled + r, num_rejected + r);\n        else\n            ref_accept(draft_ids + cu[r], tgt, k, out_tokens + base, num_sampled + r,\n                       num_rejected + r);\n        if (target_ids)\n            for (int32_t j = 0; j <= k; ++j)\n                target_ids[base + j] = tgt[j];\n    }\n}\n\n/* Ragged greedy verification from gathered",
+     "        if (prefilling && prefilling[r + 1 < n_req ? r + 1 : r])\n            ref_prefilling(k, out_tokens + base, num_sampled + r, num_rejected + r);\n        else\n            ref_accept(draft_ids + cu[r], tgt, k, out_tokens + base, num_sampled + r,\n                       num_rejected + r);\n        if (target_ids)\n            for (int32_t j = 0; j <= k; ++j)\n                target_ids[base + j] = tgt[j];\n    }\n}\n\n/* Ragged greedy verification from gathered"),
     ("map_without_draft_id",
      "? (int64_t)ids[i] + d2t[ids[i]] : -1;", "? d2t[ids[i]] : -1;"),
     ("nan_scaled_too",
