@@ -240,23 +240,30 @@ vpa_status vpa_greedy_verify(const vpa_stat* draft_stats, int32_t m_draft,
  *  draft_stats  [n_shards][total_drafts][m_draft] (row cu[r]+j = draft j of r),
  *  bonus_stats  [n_shards][n_req][m_bonus].
  *  draft_ids    int32 [total_drafts], request r's drafts at cu[r]...
+ *  prefilling   device uint8 [n_req], or NULL for none: a nonzero entry marks
+ *               a request that is still prefilling.  The PR's "Test Plan"
+ *               lists such requests without a rule; the reading here is that
+ *               one samples nothing: all K_r+1 of its out_tokens hold -1 and
+ *               num_sampled = num_rejected = 0.  Its target_ids are written
+ *               as for any request.
  *  out_tokens   out, int32 [total_drafts + n_req]: request r's K_r+1 entries
  *               at cu[r]+r (accepted drafts, then the correction or bonus
  *               token, then -1); a request with K_r = 0 emits its bonus token.
  *  num_sampled, num_rejected  out, int32 [n_req]: accepted+1 and K_r-accepted;
  *               both -1 for a request whose offsets are malformed (K_r < 0,
  *               K_r > VPA_MAX_DRAFTS, or outside [0, total_drafts]), which then
- *               writes no tokens.  Offsets that pass these checks one by
- *               one but decrease across requests make requests overlap:
- *               their outputs are then unspecified, though every access
- *               stays inside the arrays above.
+ *               writes no tokens, prefilling or not.  Offsets that pass these
+ *               checks one by one but decrease across requests make requests
+ *               overlap: their outputs are then unspecified, though every
+ *               access stays inside the arrays above.
  *  target_ids   out, int32 [total_drafts + n_req] or NULL. */
 vpa_status vpa_greedy_verify_ragged(const vpa_stat* draft_stats, int32_t m_draft,
                                     const vpa_stat* bonus_stats, int32_t m_bonus,
                                     int32_t n_shards, int64_t n_req, const int32_t* cu,
                                     int64_t total_drafts, const int32_t* draft_ids,
-                                    int32_t* out_tokens, int32_t* num_sampled,
-                                    int32_t* num_rejected, int32_t* target_ids, void* stream);
+                                    const uint8_t* prefilling, int32_t* out_tokens,
+                                    int32_t* num_sampled, int32_t* num_rejected,
+                                    int32_t* target_ids, void* stream);
 
 /* Message describing the last non-OK status returned on the calling thread
  * ("" if none).  The pointer stays valid until the next call on that thread. */

@@ -217,12 +217,12 @@ def test_ragged_rejects(lib):
     assert rr(FAKE_ODD, 3, 4, FAKE, FAKE, None) == vpa.VPA_ERR_INVALID
     assert rr(None, 0, 0, None, None, None) == vpa.VPA_OK
     gr = lib.vpa_greedy_verify_ragged
-    assert gr(FAKE, 0, FAKE, 50, 4, 3, FAKE, 6, FAKE, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
-    assert gr(FAKE, 7, FAKE, 50, 4, 3, None, 6, FAKE, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
-    assert gr(FAKE, 7, FAKE, 50, 4, 3, FAKE, 6, None, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
-    assert gr(FAKE, 7, FAKE, 50, 4, 3, FAKE, 6, FAKE, FAKE, FAKE, FAKE, FAKE_ODD, None) == vpa.VPA_ERR_INVALID
-    assert gr(FAKE, 7, FAKE, 50, 4, -2, FAKE, 6, FAKE, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
-    assert gr(None, 7, None, 50, 4, 0, None, 0, None, None, None, None, None, None) == vpa.VPA_OK
+    assert gr(FAKE, 0, FAKE, 50, 4, 3, FAKE, 6, FAKE, None, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert gr(FAKE, 7, FAKE, 50, 4, 3, None, 6, FAKE, None, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert gr(FAKE, 7, FAKE, 50, 4, 3, FAKE, 6, None, None, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert gr(FAKE, 7, FAKE, 50, 4, 3, FAKE, 6, FAKE, None, FAKE, FAKE, FAKE, FAKE_ODD, None) == vpa.VPA_ERR_INVALID
+    assert gr(FAKE, 7, FAKE, 50, 4, -2, FAKE, 6, FAKE, None, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert gr(None, 7, None, 50, 4, 0, None, 0, None, None, None, None, None, None, None) == vpa.VPA_OK
 
 
 def test_launches_beyond_one_dispatch_are_rejected(lib):
@@ -246,8 +246,8 @@ def test_launches_beyond_one_dispatch_are_rejected(lib):
                                  None) == vpa.VPA_ERR_INVALID
     assert "dispatch" in vpa.last_error()
     req = (1 << 24) + 1                          # one 256-thread workgroup per request
-    assert lib.vpa_greedy_verify_ragged(FAKE, 1, FAKE, 1, 1, req, FAKE, 0, None, FAKE, FAKE, FAKE,
-                                        None, None) == vpa.VPA_ERR_INVALID
+    assert lib.vpa_greedy_verify_ragged(FAKE, 1, FAKE, 1, 1, req, FAKE, 0, None, None, FAKE, FAKE,
+                                        FAKE, None, None) == vpa.VPA_ERR_INVALID
     assert "dispatch" in vpa.last_error()
 
 

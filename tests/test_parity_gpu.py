@@ -218,6 +218,17 @@ def test_ragged_verify(seed, vocab, s, n_req, kmax):
     got2 = vpa.verify_ragged(x, v, w, s, cud, dd, total, with_targets=False)
     for g, wv in zip(got2[:3], want[:3]):
         assert_same(g, wv, "verify_ragged")
+    # about a third of the requests still prefilling (they sample nothing)
+    pf = torch.rand(n_req, generator=torch.Generator().manual_seed(seed + 50)) < 0.35
+    want_p = oracle.greedy_verify_ragged(x_cpu, v, cu, drafts, prefilling=pf)
+    got_p = vpa.greedy_verify_ragged(dst, bst, cud, dd, total, prefilling=_dev(pf))
+    for g, wv, nm in zip(got_p, want_p, ("out_tokens", "num_sampled", "num_rejected",
+                                         "target_ids")):
+        assert_same(g, wv, f"ragged prefilling {nm}")
+    got_p2 = vpa.verify_ragged(x, v, w, s, cud, dd, total, with_targets=False,
+                               prefilling=_dev(pf.to(torch.uint8)))
+    for g, wv in zip(got_p2[:3], want_p[:3]):
+        assert_same(g, wv, "verify_ragged prefilling")
 
 
 def test_random_ragged_batches():
@@ -234,9 +245,14 @@ def test_random_ragged_batches():
         x_cpu, v, w, s, cu, drafts = _ragged_case(100 + trial, vocab, s, n_req, kmax, dtype,
                                                   p_copy=rng.random())
         total = int(cu[-1])
-        _announce(f"random ragged {trial} V={v} S={s} R={n_req} Kmax={kmax} total={total} {dtype}")
-        want = oracle.greedy_verify_ragged(x_cpu, v, cu, drafts)
-        got = vpa.verify_ragged(_dev(x_cpu), v, w, s, _dev(cu), _dev(drafts), total)
+        pf = None
+        if trial % 2:
+            pf = torch.tensor([rng.random() < 0.3 for _ in range(n_req)], dtype=torch.bool)
+        _announce(f"random ragged {trial} V={v} S={s} R={n_req} Kmax={kmax} total={total} {dtype}"
+                  f" prefilling={None if pf is None else int(pf.sum())}")
+        want = oracle.greedy_verify_ragged(x_cpu, v, cu, drafts, prefilling=pf)
+        got = vpa.verify_ragged(_dev(x_cpu), v, w, s, _dev(cu), _dev(drafts), total,
+                                prefilling=None if pf is None else _dev(pf))
         for a, b, nm in zip(got, want, ("out_tokens", "num_sampled", "num_rejected", "target_ids")):
             assert_same(a, b, f"random ragged {trial} {nm}")
 
@@ -257,6 +273,16 @@ def test_ragged_malformed_offsets_are_flagged():
     assert ns[0] >= 1 and ns[3] >= 1
     dr, br = vpa.ragged_rows(_dev(bad), total)
     assert _host(br)[1:3].tolist() == [-1, -1]
+    # malformed offsets win over a prefilling flag; a prefilling request
+    # with good offsets samples nothing
+    pf = _dev(torch.tensor([1, 1, 0, 0], dtype=torch.uint8))
+    out, ns, nr, tg = vpa.greedy_verify_ragged(dst, bst, _dev(bad), _dev(drafts), total,
+                                               prefilling=pf)
+    ns, nr, out = _host(ns), _host(nr), _host(out)
+    assert ns[:3].tolist() == [0, -1, -1] and nr[:3].tolist() == [0, -1, -1]
+    k0 = int(cu[1])
+    assert out[:k0 + 1].tolist() == [-1] * (k0 + 1)
+    assert ns[3] >= 1
 
 
 def test_row_list_out_of_range_rows_are_empty():

@@ -85,7 +85,7 @@ def _bind(lib):
     lib.vpa_ragged_rows.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.vpa_ragged_rows.restype = st
     lib.vpa_greedy_verify_ragged.argtypes = [vp, i32, vp, i32, i32, i64, vp, i64, vp, vp, vp, vp,
-                                             vp, vp]
+                                             vp, vp, vp]
     lib.vpa_greedy_verify_ragged.restype = st
     lib.vpa_last_error.argtypes = []
     lib.vpa_last_error.restype = ctypes.c_char_p
@@ -381,18 +381,34 @@ def verify_stats_rows(logits, vocab, shard_width, n_shards, draft_rows, bonus_ro
     return dst, bst
 
 
+def _prefilling_flags(prefilling, n_req, device):
+    """Optional per-request prefilling flags: a bool or uint8 device tensor [R]."""
+    if prefilling is None:
+        return None
+    if prefilling.dtype not in (torch.bool, torch.uint8) or not prefilling.is_contiguous():
+        raise ValueError("prefilling must be a contiguous bool or uint8 tensor")
+    if prefilling.device != device:
+        raise ValueError(f"prefilling is on {prefilling.device}, expected {device}")
+    if prefilling.numel() != n_req:
+        raise ValueError(f"prefilling has {prefilling.numel()} entries for {n_req} requests")
+    return prefilling
+
+
 def greedy_verify_ragged(draft_stats, bonus_stats, cu, draft_ids, total_drafts=None,
-                         with_targets=True, stream=None):
+                         with_targets=True, prefilling=None, stream=None):
     """Ragged greedy verification from statistics.  cu int32 [R+1] cumulative
-    draft counts; draft_ids int32 [total_drafts].  Returns (out_tokens
-    [total+R], num_sampled [R], num_rejected [R], target_ids [total+R] or None);
-    request r's K_r+1 outputs sit at offset cu[r]+r."""
+    draft counts; draft_ids int32 [total_drafts]; prefilling: optional bool or
+    uint8 [R], true for a request still prefilling, which samples nothing (-1
+    in its slots, 0 sampled, 0 rejected).  Returns (out_tokens [total+R],
+    num_sampled [R], num_rejected [R], target_ids [total+R] or None); request
+    r's K_r+1 outputs sit at offset cu[r]+r."""
     _stats_tensor(draft_stats, "draft_stats")
     _stats_tensor(bonus_stats, "bonus_stats")
     total = _total_drafts(cu, total_drafts)
     n_req = cu.numel() - 1
     dev = bonus_stats.device
     _int32_dev(draft_ids, "draft_ids", dev)
+    prefilling = _prefilling_flags(prefilling, n_req, dev)
     if draft_ids.numel() != total or draft_stats.shape[1] != total or bonus_stats.shape[1] != n_req:
         raise ValueError("statistics / draft_ids do not match the offsets")
     if draft_stats.shape[0] != bonus_stats.shape[0]:
@@ -403,16 +419,18 @@ def greedy_verify_ragged(draft_stats, bonus_stats, cu, draft_ids, total_drafts=N
     tg = torch.empty(total + n_req, dtype=torch.int32, device=dev) if with_targets else None
     _check(_on(dev, lib().vpa_greedy_verify_ragged, _vp(draft_stats), draft_stats.shape[2],
                _vp(bonus_stats), bonus_stats.shape[2], bonus_stats.shape[0], n_req, _vp(cu), total,
-               _vp(draft_ids), _vp(out), _vp(ns), _vp(nr), _vp(tg), _stream(stream, dev)))
+               _vp(draft_ids), _vp(prefilling), _vp(out), _vp(ns), _vp(nr), _vp(tg),
+               _stream(stream, dev)))
     return out, ns, nr, tg
 
 
 def verify_ragged(logits, vocab, shard_width, n_shards, cu, draft_ids, total_drafts=None,
                   block_draft=DRAFT_BLOCK, block_bonus=BONUS_BLOCK, with_targets=True,
-                  stream=None):
+                  prefilling=None, stream=None):
     """The whole ragged verification on one GPU: row lists, statistics, finish."""
     total = _total_drafts(cu, total_drafts)
     draft_rows, bonus_rows = ragged_rows(cu, total, stream=stream)
     dst, bst = verify_stats_rows(logits, vocab, shard_width, n_shards, draft_rows, bonus_rows,
                                  block_draft, block_bonus, stream=stream)
-    return greedy_verify_ragged(dst, bst, cu, draft_ids, total, with_targets, stream=stream)
+    return greedy_verify_ragged(dst, bst, cu, draft_ids, total, with_targets, prefilling,
+                                stream=stream)

@@ -430,8 +430,9 @@ vpa_status vpa_greedy_verify_ragged(const vpa_stat* draft_stats, int32_t m_draft
                                     const vpa_stat* bonus_stats, int32_t m_bonus,
                                     int32_t n_shards, int64_t n_req, const int32_t* cu,
                                     int64_t total_drafts, const int32_t* draft_ids,
-                                    int32_t* out_tokens, int32_t* num_sampled,
-                                    int32_t* num_rejected, int32_t* target_ids, void* stream) {
+                                    const uint8_t* prefilling, int32_t* out_tokens,
+                                    int32_t* num_sampled, int32_t* num_rejected,
+                                    int32_t* target_ids, void* stream) {
     if (n_shards < 1 || m_draft < 1 || m_bonus < 1 || (int64_t)n_shards * m_draft > INT32_MAX ||
         (int64_t)n_shards * m_bonus > INT32_MAX)
         return fail(VPA_ERR_INVALID, "n_shards %d / m_draft %d / m_bonus %d invalid",
@@ -455,8 +456,8 @@ vpa_status vpa_greedy_verify_ragged(const vpa_stat* draft_stats, int32_t m_draft
         return st;
     hipError_t e = vpa::launch_greedy_verify_ragged(
         draft_stats, m_draft, bonus_stats, m_bonus, n_shards, (int32_t)n_req, cu,
-        (int32_t)total_drafts, draft_ids, out_tokens, num_sampled, num_rejected, target_ids,
-        (hipStream_t)stream);
+        (int32_t)total_drafts, draft_ids, prefilling, out_tokens, num_sampled, num_rejected,
+        target_ids, (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "vpa_greedy_verify_ragged launch");
 }
 

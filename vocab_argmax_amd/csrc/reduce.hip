@@ -149,13 +149,16 @@ __global__ __launch_bounds__(kThreads) void ragged_rows_kernel(const int32_t* __
 // Ragged verification: one workgroup per request r with K_r = cu[r+1]-cu[r]
 // drafts; the wavefronts share out the K_r+1 positions as in the uniform
 // kernel, then one lane applies the acceptance and writes K_r+1 outputs at
-// offset cu[r]+r.
+// offset cu[r]+r.  A request flagged in `prefilling` (vLLM PR #62604, "Test
+// Plan", lists such requests; read here as sampling nothing) writes -1 in
+// all its slots and 0 sampled / 0 rejected; its targets are still written.
 __global__ __launch_bounds__(kThreads) void greedy_verify_ragged_kernel(
     const vpa_stat* __restrict__ draft_stats, int32_t m_draft,
     const vpa_stat* __restrict__ bonus_stats, int32_t m_bonus, int32_t n_shards, int32_t n_req,
     const int32_t* __restrict__ cu, int32_t total, const int32_t* __restrict__ draft_ids,
-    int32_t* __restrict__ out_tokens, int32_t* __restrict__ num_sampled,
-    int32_t* __restrict__ num_rejected, int32_t* __restrict__ target_ids) {
+    const uint8_t* __restrict__ prefilling, int32_t* __restrict__ out_tokens,
+    int32_t* __restrict__ num_sampled, int32_t* __restrict__ num_rejected,
+    int32_t* __restrict__ target_ids) {
     __shared__ int32_t targets[VPA_MAX_DRAFTS + 1];
     const int lane = threadIdx.x & 63;
     const int32_t wave = __builtin_amdgcn_readfirstlane((int32_t)(threadIdx.x >> 6));
@@ -185,6 +188,13 @@ __global__ __launch_bounds__(kThreads) void greedy_verify_ragged_kernel(
     }
     __syncthreads();
     if (threadIdx.x == 0) {
+        if (prefilling && prefilling[r]) {
+            for (int32_t j = 0; j <= k; ++j)
+                out_tokens[base + j] = -1;
+            num_sampled[r] = 0;
+            num_rejected[r] = 0;
+            return;
+        }
         const int32_t* drafts = draft_ids + lo;
         int32_t n = 0;
         while (n < k && drafts[n] == targets[n])
@@ -222,12 +232,12 @@ hipError_t launch_greedy_verify_ragged(const vpa_stat* draft_stats, int32_t m_dr
                                        const vpa_stat* bonus_stats, int32_t m_bonus,
                                        int32_t n_shards, int32_t n_req, const int32_t* cu,
                                        int32_t total_drafts, const int32_t* draft_ids,
-                                       int32_t* out_tokens, int32_t* num_sampled,
-                                       int32_t* num_rejected, int32_t* target_ids,
-                                       hipStream_t stream) {
+                                       const uint8_t* prefilling, int32_t* out_tokens,
+                                       int32_t* num_sampled, int32_t* num_rejected,
+                                       int32_t* target_ids, hipStream_t stream) {
     return launch(greedy_verify_ragged_kernel, dim3((unsigned)n_req), dim3(kThreads), 0, stream,
                   draft_stats, m_draft, bonus_stats, m_bonus, n_shards, n_req, cu, total_drafts,
-                  draft_ids, out_tokens, num_sampled, num_rejected, target_ids);
+                  draft_ids, prefilling, out_tokens, num_sampled, num_rejected, target_ids);
 }
 
 hipError_t launch_combine(const vpa_stat* stats, int32_t n_shards, int32_t n_rows, int32_t m,
