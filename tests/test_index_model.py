@@ -1,0 +1,170 @@
+"""A CPU model of the statistics kernel's index arithmetic
+(vocab_argmax_amd/csrc/block_stats.hip), checked over random geometries:
+
+- the item decode covers every (row, shard, slot) of a launch exactly once
+  and every statistic index lies inside [0, n_local * n_rows * M);
+- within a segment, the edge elements read one by one and the 16-byte
+  vectors of the pipelined scan (clamped chunk indices) touch only the
+  segment's valid columns of its row, and cover them exactly;
+- every vector address is 16-byte aligned, whatever the buffer's offset;
+- the positions the fold packs decode back to the column that was loaded.
+
+The model restates the kernel's integer formulas; it shares no code with
+the library (none could be shared: the kernel is device code).  A change to
+the kernel's indexing has to be carried over here.
+"""
+import random
+
+import pytest
+
+LANE_ITERS = 16            # VPA_LANE_ITERS
+PIPE = {2: 8, 4: 16}       # VPA_PIPE_BF16, VPA_PIPE_F32
+
+
+def slots(w, s, b):
+    return max((i * w + w - 1) // b - (i * w) // b + 1 for i in range(s))
+
+
+def lanes_log2(block, shard_width, esize):
+    span = min(block, shard_width)
+    vectors = (span * esize + 15) // 16 + 1
+    lg = 3
+    while lg < 6 and (1 << (lg + 1)) * LANE_ITERS <= vectors:
+        lg += 1
+    return lg
+
+
+def decode_item(item, m, n_local):
+    j = item % m
+    rest = item // m
+    return rest // n_local, rest % n_local, j          # (i, sl, j)
+
+
+def segment_range(first_shard, sl, j, w, block, vocab):
+    shard_lo = (first_shard + sl) * w
+    blo = (shard_lo // block + j) * block
+    lo = max(blo, shard_lo)
+    hi = min(blo + block, shard_lo + w, vocab)
+    return lo, hi
+
+
+def scan_segment(esize, base_mod16, row, ld, col0, lo, hi, lanes):
+    """Columns the group of `lanes` lanes reads for segment [lo, hi), with
+    checks on every index; returns the multiset of columns as a list."""
+    vec = 16 // esize
+    mis = base_mod16 // esize
+    a_lo = row * ld + (lo - col0) + mis
+    d = lo - a_lo
+    qa = -(-a_lo // vec)
+    qb = (a_lo + (hi - lo)) // vec
+    if qa < qb:
+        head_end, tail_lo = qa * vec + d, qb * vec + d
+    else:
+        head_end, tail_lo, qb = hi, hi, qa
+    cols = []
+    for gl in range(lanes):                       # edge elements, one by one
+        c = lo + gl
+        while c < head_end:
+            cols.append(c)
+            c += lanes
+        c = tail_lo + gl
+        while c < hi:
+            cols.append(c)
+            c += lanes
+    n = qb - qa
+    if n > 0:
+        u_deep = PIPE[esize]
+        nit = -(-n // lanes)
+        chunks = -(-nit // u_deep)
+        c0 = qa * vec + d
+        seen = set()
+        for gl in range(lanes):
+            for ch in range(chunks):
+                i0 = gl + lanes * u_deep * ch
+                for u in range(u_deep):
+                    i = min(i0 + lanes * u, n - 1)           # load_clamped
+                    assert 0 <= i < n
+                    # byte address modulo 16: the kernel steps back `mis`
+                    # elements from the buffer base, then adds whole vectors
+                    addr = base_mod16 - mis * esize + (qa + i) * 16
+                    assert addr % 16 == 0
+                    # fold: the packed position decodes to the loaded vector
+                    for e in range(vec):
+                        pos = u * vec + e
+                        i_dec = min(i0 + lanes * (pos // vec), n - 1)
+                        assert i_dec == i
+                        col = c0 + i_dec * vec + pos % vec
+                        assert col == (qa + i) * vec + e + d
+                    seen.add(i)
+        for i in seen:
+            cols.extend((qa + i) * vec + e + d for e in range(vec))
+    # the buffer element of each column lies inside its row's valid part
+    for c in cols:
+        assert lo <= c < hi, (lo, hi, c)
+        elem = row * ld + (c - col0)
+        assert row * ld <= elem < row * ld + ld
+    return cols
+
+
+def check_launch(rng, esize):
+    s = rng.choice([1, 2, 3, 4, 5, 8])
+    vocab = rng.choice([1, 2, 7, 63, 1000, 4097, 50257, 70001, 151936, 200064])
+    w = -(-vocab // s) + rng.choice([0, 0, 1, 3, 64])
+    block = rng.choice([1, 3, 64, 255, 256, 1000, 1024, 2048, 4096, 8192, 65536, 1 << 20])
+    if vocab > 5000 and block < 256:
+        block = 256
+    first = rng.randrange(s)
+    n_local = rng.randint(1, s - first)
+    col0 = first * w
+    need = min(n_local * w, vocab - col0)
+    ld = max(need, 1) + rng.choice([0, 0, 1, 5, 8, 128])
+    base_mod16 = rng.choice([0, esize, 2 * esize, 16 - esize, 6 if esize == 2 else 12])
+    m = slots(w, s, block)
+    n_rows = rng.choice([1, 2, 3])
+    lg = lanes_log2(block, w, esize)
+    lanes = 1 << lg
+    per_wave = 64 // lanes
+    n_items = n_rows * n_local * m
+    n_waves = -(-n_items // per_wave)
+    seen_items, stat_idx = set(), set()
+    segments = 0
+    for wave in range(n_waves):
+        for g in range(per_wave):
+            item = wave * per_wave + g
+            if item >= n_items:
+                continue
+            seen_items.add(item)
+            i, sl, j = decode_item(item, m, n_local)
+            idx = (sl * n_rows + i) * m + j
+            assert 0 <= idx < n_local * n_rows * m
+            stat_idx.add(idx)
+            lo, hi = segment_range(first, sl, j, w, block, vocab)
+            if lo >= hi:
+                continue
+            row = i
+            cols = scan_segment(esize, base_mod16, row, ld, col0, lo, hi, lanes)
+            assert sorted(cols) == list(range(lo, hi))     # each column exactly once
+            segments += 1
+    assert seen_items == set(range(n_items))
+    assert len(stat_idx) == n_items
+    return segments
+
+
+@pytest.mark.parametrize("esize", [2, 4])
+def test_statistics_kernel_index_arithmetic(esize):
+    rng = random.Random(1000 + esize)
+    segments = 0
+    for _ in range(120):
+        segments += check_launch(rng, esize)
+    assert segments > 1000
+
+
+def test_model_matches_the_kernel_constants():
+    """The constants the model assumes are the ones the kernel source sets."""
+    import os
+    src = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "vocab_argmax_amd", "csrc", "block_stats.hip")).read()
+    assert "#define VPA_LANE_ITERS 16" in src
+    assert "#define VPA_PIPE_BF16 8" in src
+    assert "#define VPA_PIPE_F32 16" in src
+    assert "i = i < ilast ? i : ilast;" in src            # clamped chunk indices
