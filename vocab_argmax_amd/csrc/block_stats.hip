@@ -14,11 +14,12 @@
 // workgroup, no LDS and no barriers.  The loads come in chunks of U group
 // iterations, software-pipelined: chunk c+1 is issued before chunk c is
 // folded, so a wavefront keeps U to 2U loads in flight.  U = 8 for bf16
-// (91 VGPRs, 5 wavefronts per SIMD) and 16 for fp32 (150 VGPRs, held to 2
-// wavefronts per SIMD by the launch's LDS reservation) measured fastest on
-// MI355X.  Each lane keeps a running best, and a shuffle reduction inside
-// the group finishes the segment.  Consecutive groups and wavefronts take
-// consecutive segments of a row, so a wavefront reads contiguous memory.
+// (91 VGPRs) and 16 for fp32 (150 VGPRs) measured fastest on MI355X, with
+// the launch's LDS reservation holding a CU to 4 wavefronts per SIMD for
+// bf16 and 2 for fp32.  Each lane keeps a running best, and a shuffle
+// reduction inside the group finishes the segment.  Consecutive groups and
+// wavefronts take consecutive segments of a row, so a wavefront reads
+// contiguous memory.
 // Padding columns [V, S*W) are never read.
 //
 // Per-lane scan.  Every element becomes an order-preserving unsigned key
@@ -58,11 +59,13 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kLaneIters = VPA_LANE_ITERS;   // target iterations per lane of a segment
 
 // LDS reserved per workgroup at launch and never touched by the kernel, by
-// element size.  bf16: 32 KiB lets LDS alone hold a CU to 5 workgroups
-// (20 wavefronts), the count the registers allow too; on MI355X the
-// statistics launches measured 2-3 % faster with it than with no or smaller
-// reservations.  fp32 (150 VGPRs, 3 workgroups per CU by registers): 64 KiB,
-// 2 workgroups per CU, measured 2-3 % faster than 32 or 48 KiB.
+// element size; it sets how many workgroups share a CU.  bf16: with
+// 32 KiB, at most 4 workgroups (16 wavefronts) run per CU on MI355X, where
+// the registers would allow 5; per-wavefront timestamps show no more than
+// 16 resident wavefronts per CU.  That residency measured 2-3 % faster than
+// 5 per CU (no or smaller reservations) and faster than 3 or 2.  fp32
+// (150 VGPRs, 3 workgroups per CU by registers): 64 KiB, 2 workgroups per
+// CU, measured 2-3 % faster than 32 or 48 KiB.
 #ifndef VPA_LDS_RESERVE_KB
 #define VPA_LDS_RESERVE_KB 32
 #endif
