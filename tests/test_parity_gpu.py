@@ -129,6 +129,65 @@ def test_verify_many_drafts(k):
     _verify_both(x, vocab, w, s, n_req, k, drafts, 256, 64, f"many drafts K={k}")
 
 
+def test_verify_at_the_draft_limit():
+    """K = VPA_MAX_DRAFTS (4096), uniform and ragged: one request with every
+    draft accepted (bonus token at position K), one rejected deep inside;
+    a ragged batch with a 4096-draft request, a zero-draft request and a
+    request still prefilling."""
+    k, vocab, s = 4096, 50, 2
+    w = vocab // s
+    n_req = 2
+    g = torch.Generator().manual_seed(4096)
+    x = (torch.randn((n_req * (k + 1), s * w), generator=g) * 2).to(torch.bfloat16)
+    tgt, _ = oracle.argmax(x, vocab)
+    targets = tgt.reshape(n_req, k + 1)
+    plan = torch.ones((n_req, k), dtype=torch.int8)
+    plan[1, 3000] = 0
+    uniform = torch.zeros((n_req, k), dtype=torch.int32)
+    uniform[1, 3000] = (int(targets[1, 3000]) + 1) % vocab      # a sure mismatch
+    drafts = workloads.compose_drafts(targets, plan, uniform)
+    want = _verify_both(x, vocab, w, s, n_req, k, drafts, 256, 16, "draft limit")
+    assert want[1].tolist() == [k + 1, 3001]
+    # ragged: K_r = 4096, 0, 5; the last request is still prefilling
+    cu = torch.tensor([0, k, k, k + 5], dtype=torch.int32)
+    total = int(cu[-1])
+    xr = (torch.randn((total + 3, s * w), generator=g) * 2).to(torch.bfloat16)
+    tr, _ = oracle.argmax(xr, vocab)
+    draft_rows, _ = oracle.ragged_rows(cu)
+    dr = tr[draft_rows.long()].to(torch.int32)
+    dr[1234] = (int(dr[1234]) + 1) % vocab
+    pf = torch.tensor([0, 0, 1], dtype=torch.uint8)
+    _announce(f"ragged draft limit total={total}")
+    want_r = oracle.greedy_verify_ragged(xr, vocab, cu, dr, prefilling=pf)
+    got_r = vpa.verify_ragged(_dev(xr), vocab, w, s, _dev(cu), _dev(dr), total,
+                              prefilling=_dev(pf))
+    for a, b, nm in zip(got_r, want_r, ("out_tokens", "num_sampled", "num_rejected",
+                                        "target_ids")):
+        assert_same(a, b, f"ragged draft limit {nm}")
+    assert want_r[1].tolist() == [1235, 1, 0]
+
+
+def test_one_column_shards_and_more_shards_than_columns():
+    """Degenerate shard geometries: one column per shard (S = V = 1000,
+    W = 1), and more shards than valid columns (S = 1500, W = 1: shards past
+    V hold only padding and give empty statistics), at blocks of 1, 7 and
+    8192 columns, in both dtypes."""
+    for dtype in (torch.bfloat16, torch.float32):
+        for vocab, s in ((1000, 1000), (1000, 1500)):
+            x_cpu = oracle_pins._special_matrix(5, s, 7000 + s, dtype)
+            x_cpu[:, vocab:] = float("nan")
+            x = _dev(x_cpu)
+            want_ids, want_vals = oracle.argmax(x_cpu, vocab)
+            for block in (1, 7, 8192):
+                name = f"one-column shards V={vocab} S={s} B={block} {dtype}"
+                _announce(name)
+                assert_same(vpa.block_stats(x, vocab, 1, s, block),
+                            oracle.block_stats(x_cpu, vocab, 1, s, block), name)
+                ids, vals = vpa.top_tokens(x, vocab, 1, s, block)
+                assert_same(ids, want_ids, name + " ids")
+                assert_same(vals.to(torch.int64) & 0xFFFFFFFF, want_vals, name + " vals")
+
+
 @pytest.mark.parametrize("scale", [1.0, 0.7, 1 / 0.7, 1e-40, 3e38])
 def test_epilogue_d2t_and_scale(scale):
     """top_tokens and combine_stats with a draft-to-target table and a positive
