@@ -154,7 +154,7 @@ def check_launch(rng, esize):
 def test_statistics_kernel_index_arithmetic(esize):
     rng = random.Random(1000 + esize)
     segments = 0
-    for _ in range(120):
+    for _ in range(80):
         segments += check_launch(rng, esize)
     assert segments > 1000
 
