@@ -30,9 +30,10 @@
  * with one collective and run the combining calls unchanged.
  *
  * Conventions shared by every call:
- *  - Pointers named logits, stats, ids, val_bits, draft_ids, out_tokens,
- *    num_sampled, num_rejected, target_ids, rows and workspace are DEVICE
- *    memory owned by the caller.  The library never allocates or frees.
+ *  - Pointers named logits, stats, ids, val_bits, mapped, d2t, draft_ids,
+ *    out_tokens, num_sampled, num_rejected, target_ids, rows, draft_rows,
+ *    bonus_rows, cu, prefilling and workspace are DEVICE memory owned by the
+ *    caller.  The library never allocates or frees.
  *  - Every call only enqueues work on `stream` (a hipStream_t passed as
  *    void*; NULL is the default stream) and returns without synchronising;
  *    outputs are defined once the stream reaches that point.
