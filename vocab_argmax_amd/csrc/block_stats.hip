@@ -11,9 +11,9 @@
 // lanes of one wavefront (L = 64 for 8192-column bf16 blocks, down to 8 for
 // 1024-column ones), so a lane makes about 16 iterations of 16-byte
 // non-temporal loads whatever the block size; four wavefronts per
-// workgroup, no LDS and no barriers.  The loads come in chunks of U group
-// iterations, software-pipelined: chunk c+1 is issued before chunk c is
-// folded, so a wavefront keeps U to 2U loads in flight.  U = 8 for bf16
+// workgroup, no LDS accesses and no barriers.  The loads come in chunks of
+// U group iterations, software-pipelined: chunk c+1 is issued before chunk
+// c is folded, so a wavefront keeps U to 2U loads in flight.  U = 8 for bf16
 // (91 VGPRs) and 16 for fp32 (150 VGPRs) measured fastest on MI355X, with
 // the launch's LDS reservation holding a CU to 4 wavefronts per SIMD for
 // bf16 and 2 for fp32.  Each lane keeps a running best, and a shuffle
