@@ -628,6 +628,30 @@ def test_top_tokens_workspace_reused_across_shapes():
         assert_same(vals.to(torch.int64) & 0xFFFFFFFF, want_vals, f"{name} B={b} vals")
 
 
+def test_top_tokens_rejects_bad_output_tensors():
+    """Caller-supplied outputs are checked before any launch: wrong dtype,
+    wrong length or a non-contiguous workspace raise, and nothing is written."""
+    x = _dev(oracle_pins._special_matrix(4, 1000, 99, torch.bfloat16))
+    n = 4
+    good = dict(ids=torch.zeros(n, dtype=torch.int32, device=DEV),
+                val_bits=torch.zeros(n, dtype=torch.int32, device=DEV))
+    bad = [dict(ids=torch.zeros(n, dtype=torch.int64, device=DEV)),
+           dict(ids=torch.zeros(n - 1, dtype=torch.int32, device=DEV)),
+           dict(val_bits=torch.zeros(2 * n, dtype=torch.int32, device=DEV)[::2]),
+           dict(d2t=torch.zeros(1000, dtype=torch.int64, device=DEV),
+                mapped=torch.zeros(n, dtype=torch.int32, device=DEV)),
+           dict(workspace=torch.zeros((2, 4096), dtype=torch.uint8, device=DEV)[:, ::2])]
+    for kw in bad:
+        args = dict(good)
+        args.update(kw)
+        with pytest.raises(ValueError):
+            vpa.top_tokens(x, 1000, 250, 4, 256, **args)
+    torch.cuda.synchronize()
+    assert int(good["ids"].abs().sum()) == 0          # nothing was launched
+    ids, _ = vpa.top_tokens(x, 1000, 250, 4, 256, **good)
+    assert_same(ids, oracle.argmax(x.cpu(), 1000)[0], "good outputs")
+
+
 def test_two_streams_run_concurrently():
     """The library keeps no device state between calls: two streams each run
     the draft argmax and the verification on their own data, interleaved

@@ -175,6 +175,15 @@ def _stats_tensor(t, name):
     return t
 
 
+def _out_tensor(t, name, dtype, n, device):
+    """A caller-supplied output: contiguous, of `dtype`, n elements, on `device`."""
+    if t.dtype != dtype or not t.is_contiguous() or t.numel() != n:
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of {n} elements")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t
+
+
 def stats_slots(shard_width: int, n_shards: int, block: int) -> int:
     """M: statistic slots per shard (the most global blocks a shard touches)."""
     m = lib().vpa_stats_slots(shard_width, n_shards, block)
@@ -288,15 +297,18 @@ def top_tokens(logits, vocab, shard_width, n_shards, block=DRAFT_BLOCK, workspac
     ld = _logits_ld(logits)
     n = logits.shape[0]
     need = top_tokens_workspace(vocab, shard_width, n_shards, n, block)
+    dev = logits.device
     if workspace is None:
-        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=logits.device)
-    if ids is None:
-        ids = torch.empty(n, dtype=torch.int32, device=logits.device)
-    if val_bits is None:
-        val_bits = torch.empty(n, dtype=torch.int32, device=logits.device)
-    if d2t is not None and mapped is None:
-        mapped = torch.empty(n, dtype=torch.int64, device=logits.device)
-    _same_device(logits.device, workspace=workspace, ids=ids, val_bits=val_bits, mapped=mapped)
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=dev)
+    elif not workspace.is_contiguous() or workspace.device != dev:
+        raise ValueError(f"workspace must be a contiguous tensor on {dev}")
+    ids = (torch.empty(n, dtype=torch.int32, device=dev) if ids is None
+           else _out_tensor(ids, "ids", torch.int32, n, dev))
+    val_bits = (torch.empty(n, dtype=torch.int32, device=dev) if val_bits is None
+                else _out_tensor(val_bits, "val_bits", torch.int32, n, dev))
+    if d2t is not None:
+        mapped = (torch.empty(n, dtype=torch.int64, device=dev) if mapped is None
+                  else _out_tensor(mapped, "mapped", torch.int64, n, dev))
     epi, _keep = _epilogue(d2t, scale, logits.device)
     _check(_on(logits.device, lib().vpa_top_tokens, _vp(logits), _dtype_code(logits), ld,
                Vocab(vocab, shard_width, n_shards), n, block, _vp(workspace),
