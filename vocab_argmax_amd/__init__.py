@@ -419,6 +419,7 @@ def greedy_verify_ragged(draft_stats, bonus_stats, cu, draft_ids, total_drafts=N
     total = _total_drafts(cu, total_drafts)
     n_req = cu.numel() - 1
     dev = bonus_stats.device
+    _same_device(dev, cu=cu, draft_stats=draft_stats)
     _int32_dev(draft_ids, "draft_ids", dev)
     prefilling = _prefilling_flags(prefilling, n_req, dev)
     if draft_ids.numel() != total or draft_stats.shape[1] != total or bonus_stats.shape[1] != n_req:
