@@ -351,6 +351,7 @@ def main():
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBPS,
             "traffic": traffic,
+            "traffic_gbps": None if traffic is None else traffic / vs_s / 1e9,
             "algorithmic_bytes_per_launch": alg["verify_stats"],
             "avg_launch_us": vs_s * 1e6,
         },
