@@ -712,6 +712,53 @@ def test_explicit_stream_argument():
         assert torch.equal(a.cpu(), b)
 
 
+def test_side_stream_temporaries_are_not_handed_out_early():
+    """Temporaries a call frees before its kernels have run (top_tokens'
+    workspace, verify_ragged's row lists and statistics) come from the given
+    stream's pool: a same-size allocation filled on the default stream while
+    the side stream is still busy cannot overwrite them."""
+    w = workloads.config3()
+    v, wd, s, r, k = w.vocab, w.shard_width, w.n_shards, w.n_req, w.k
+    x = _dev(w.logits)
+    n = x.shape[0]
+    tgt, vals = oracle.argmax(w.logits, v)
+    cu = torch.arange(0, (r + 1) * k, k, dtype=torch.int32)
+    drafts = workloads.compose_drafts(tgt.reshape(r, k + 1), w.draft_plan, w.draft_uniform)
+    want = oracle.greedy_verify_ragged(w.logits, v, cu, drafts.reshape(-1))
+    busy = torch.empty(1 << 28, dtype=torch.uint8, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        for _ in range(16):                      # keeps the side stream busy for about 1 ms
+            busy.fill_(1)
+    ids, vb = vpa.top_tokens(x, v, wd, s, 8192, stream=side)
+    out = vpa.verify_ragged(x, v, wd, s, _dev(cu), _dev(drafts.reshape(-1)), r * k, stream=side)
+    # the sizes of every temporary above, allocated and filled on the default stream
+    junk = [torch.empty(max(vpa.top_tokens_workspace(v, wd, s, n, 8192), 8), dtype=torch.uint8,
+                        device=DEV),
+            torch.empty(r * k + r, dtype=torch.int32, device=DEV),
+            torch.empty(s * (r * k * vpa.stats_slots(wd, s, 8192) + r * vpa.stats_slots(wd, s, 1024))
+                        * 2, dtype=torch.int32, device=DEV)]
+    for t in junk:
+        t.fill_(-1)
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(ids.cpu(), tgt)
+    assert torch.equal(vb.cpu().to(torch.int64) & 0xFFFFFFFF, vals)
+    for a, b, nm in zip(out, want, ("out_tokens", "num_sampled", "num_rejected", "target_ids")):
+        assert torch.equal(a.cpu(), b), nm
+
+
+def test_verify_ragged_needs_the_rows_the_requests_own():
+    """verify_ragged refuses logits with fewer rows than cu[-1] + R."""
+    x = torch.zeros((6, 1000), dtype=torch.bfloat16, device=DEV)
+    cu = torch.tensor([0, 2, 5], dtype=torch.int32, device=DEV)     # 5 drafts + 2 bonus rows = 7
+    drafts = torch.zeros(5, dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError, match="own 7"):
+        vpa.verify_ragged(x, 1000, 500, 2, cu, drafts, 5)
+
+
 def test_stale_runtime_error_is_left_to_its_owner():
     """A failed, unrelated HIP runtime call earlier in the process (here an
     invalid device number, a host-side argument error) neither fails the

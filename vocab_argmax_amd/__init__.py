@@ -19,6 +19,7 @@ fused get_top_tokens, greedy verification) and "Test Plan" (rank-order
 layout of the statistics).
 """
 import ctypes
+import functools
 import os
 
 import torch
@@ -113,17 +114,39 @@ def _check(status):
 
 
 def _vp(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
+
+
+def _raw_stream(device):
+    """Handle of `device`'s current HIP stream, as an integer."""
+    return torch._C._cuda_getCurrentRawStream(device.index if device.index is not None
+                                              else torch.cuda.current_device())
 
 
 def _stream(stream, device):
     """The HIP stream to enqueue on: the given torch stream, else the current
     stream of `device` (the device the call's tensors live on)."""
     if stream is None:
-        stream = torch.cuda.current_stream(device)
-    elif stream.device != device:
+        return _raw_stream(device)
+    if stream.device != device:
         raise ValueError(f"stream belongs to {stream.device}, the tensors to {device}")
-    return ctypes.c_void_p(stream.cuda_stream)
+    return stream.cuda_stream
+
+
+def _stream_arg(fn):
+    """Run `fn` with its `stream` argument, when one is given, as the current
+    stream.  Every tensor the call allocates (outputs, the top_tokens workspace,
+    the row lists and statistics of verify_ragged) then comes from that
+    stream's pool, and the caching allocator hands a freed temporary's memory
+    only to later work on the same stream, which runs after the kernels that
+    used it."""
+    @functools.wraps(fn)
+    def call(*args, stream=None, **kwargs):
+        if stream is None:
+            return fn(*args, **kwargs)
+        with torch.cuda.stream(stream):
+            return fn(*args, stream=stream, **kwargs)
+    return call
 
 
 def _on(device, fn, *args):
@@ -184,6 +207,7 @@ def _out_tensor(t, name, dtype, n, device):
     return t
 
 
+@functools.lru_cache(maxsize=256)
 def stats_slots(shard_width: int, n_shards: int, block: int) -> int:
     """M: statistic slots per shard (the most global blocks a shard touches)."""
     m = lib().vpa_stats_slots(shard_width, n_shards, block)
@@ -192,34 +216,43 @@ def stats_slots(shard_width: int, n_shards: int, block: int) -> int:
     return m
 
 
+@functools.lru_cache(maxsize=256)
+def _vocab(vocab, shard_width, n_shards):
+    return Vocab(vocab, shard_width, n_shards)
+
+
+@_stream_arg
 def block_stats(logits, vocab, shard_width, n_shards, block, rows=None, first_shard=0,
-                n_local=None, out=None, stream=None):
+                n_local=None, out=None, *, stream=None):
     """Per-block statistics of shards first_shard..first_shard+n_local-1.
 
     logits [R, ld]: column 0 is global column first_shard*W.  rows: optional
     int32 device tensor of row indices.  Returns int32 [n_local][n_rows][M][2].
     """
     ld = _logits_ld(logits)
+    dev = logits.device
     if n_local is None:
         n_local = n_shards - first_shard
     if rows is not None:
-        rows = _int32_dev(rows, "rows", logits.device)
+        rows = _int32_dev(rows, "rows", dev)
     n_rows = logits.shape[0] if rows is None else rows.numel()
     m = stats_slots(shard_width, n_shards, block)
     if out is None:
-        out = torch.empty((n_local, n_rows, m, 2), dtype=torch.int32, device=logits.device)
+        out = torch.empty((n_local, n_rows, m, 2), dtype=torch.int32, device=dev)
     _stats_tensor(out, "out")
-    _same_device(logits.device, out=out)
+    _same_device(dev, out=out)
     if tuple(out.shape) != (n_local, n_rows, m, 2):
         raise ValueError(f"out has shape {tuple(out.shape)}, expected {(n_local, n_rows, m, 2)}")
-    _check(_on(logits.device, lib().vpa_block_stats, _vp(logits), _dtype_code(logits), ld,
-               Vocab(vocab, shard_width, n_shards), first_shard, n_local, _vp(rows), n_rows,
-               logits.shape[0], block, _vp(out), _stream(stream, logits.device)))
+    _check(_on(dev, lib().vpa_block_stats, logits.data_ptr(), _dtype_code(logits), ld,
+               _vocab(vocab, shard_width, n_shards), first_shard, n_local, _vp(rows), n_rows,
+               logits.shape[0], block, out.data_ptr(), _stream(stream, dev)))
     return out
 
 
+@_stream_arg
 def verify_stats(logits, vocab, shard_width, n_shards, n_req, k, block_draft=DRAFT_BLOCK,
-                 block_bonus=BONUS_BLOCK, first_shard=0, n_local=None, out=None, stream=None):
+                 block_bonus=BONUS_BLOCK, first_shard=0, n_local=None, out=None, *,
+                 stream=None):
     """Draft- and bonus-row statistics of a verification batch in one launch.
 
     Request r owns rows r*(K+1)..r*(K+1)+K of logits.  Returns
@@ -227,6 +260,7 @@ def verify_stats(logits, vocab, shard_width, n_shards, n_req, k, block_draft=DRA
     `out` may supply that pair preallocated.
     """
     ld = _logits_ld(logits)
+    dev = logits.device
     if n_local is None:
         n_local = n_shards - first_shard
     if logits.shape[0] < n_req * (k + 1):
@@ -234,19 +268,22 @@ def verify_stats(logits, vocab, shard_width, n_shards, n_req, k, block_draft=DRA
     md = stats_slots(shard_width, n_shards, block_draft)
     mb = stats_slots(shard_width, n_shards, block_bonus)
     if out is None:
-        dst = torch.empty((n_local, n_req * k, md, 2), dtype=torch.int32, device=logits.device)
-        bst = torch.empty((n_local, n_req, mb, 2), dtype=torch.int32, device=logits.device)
+        # one allocation for both: draft statistics first, then bonus statistics
+        nd = n_local * n_req * k * md * 2
+        buf = torch.empty(nd + n_local * n_req * mb * 2, dtype=torch.int32, device=dev)
+        dst = buf[:nd].view(n_local, n_req * k, md, 2)
+        bst = buf[nd:].view(n_local, n_req, mb, 2)
     else:
         dst, bst = out
         if (tuple(dst.shape) != (n_local, n_req * k, md, 2)
                 or tuple(bst.shape) != (n_local, n_req, mb, 2)):
             raise ValueError("preallocated verification statistics have the wrong shape")
-    _stats_tensor(dst, "draft_stats")
-    _stats_tensor(bst, "bonus_stats")
-    _same_device(logits.device, draft_stats=dst, bonus_stats=bst)
-    _check(_on(logits.device, lib().vpa_verify_stats, _vp(logits), _dtype_code(logits), ld,
-               Vocab(vocab, shard_width, n_shards), first_shard, n_local, n_req, k, block_draft,
-               block_bonus, _vp(dst), _vp(bst), _stream(stream, logits.device)))
+        _stats_tensor(dst, "draft_stats")
+        _stats_tensor(bst, "bonus_stats")
+        _same_device(dev, draft_stats=dst, bonus_stats=bst)
+    _check(_on(dev, lib().vpa_verify_stats, logits.data_ptr(), _dtype_code(logits), ld,
+               _vocab(vocab, shard_width, n_shards), first_shard, n_local, n_req, k, block_draft,
+               block_bonus, dst.data_ptr(), bst.data_ptr(), _stream(stream, dev)))
     return dst, bst
 
 
@@ -264,7 +301,8 @@ def _epilogue(d2t, scale, device):
     return ctypes.pointer(e), d2t
 
 
-def combine_stats(stats, d2t=None, scale=1.0, stream=None):
+@_stream_arg
+def combine_stats(stats, d2t=None, scale=1.0, *, stream=None):
     """Rank-order combination of [S][N][M][2] statistics.
 
     Returns (ids int32[N], val_bits int32[N]), plus mapped int64[N] = k + d2t[k]
@@ -272,21 +310,23 @@ def combine_stats(stats, d2t=None, scale=1.0, stream=None):
     ids and scales the reported maxima (fp32, round to nearest)."""
     _stats_tensor(stats, "stats")
     s, n, m, _ = stats.shape
-    ids = torch.empty(n, dtype=torch.int32, device=stats.device)
-    vals = torch.empty(n, dtype=torch.int32, device=stats.device)
-    mapped = torch.empty(n, dtype=torch.int64, device=stats.device) if d2t is not None else None
-    epi, _keep = _epilogue(d2t, scale, stats.device)
-    _check(_on(stats.device, lib().vpa_combine_stats, _vp(stats), s, n, m, epi, _vp(ids), _vp(vals),
-               _vp(mapped), _stream(stream, stats.device)))
+    dev = stats.device
+    buf = torch.empty((2, n), dtype=torch.int32, device=dev)
+    ids, vals = buf[0], buf[1]
+    mapped = torch.empty(n, dtype=torch.int64, device=dev) if d2t is not None else None
+    epi, _keep = _epilogue(d2t, scale, dev)
+    _check(_on(dev, lib().vpa_combine_stats, stats.data_ptr(), s, n, m, epi, ids.data_ptr(),
+               vals.data_ptr(), _vp(mapped), _stream(stream, dev)))
     return (ids, vals) if d2t is None else (ids, vals, mapped)
 
 
 def top_tokens_workspace(vocab, shard_width, n_shards, n_rows, block=DRAFT_BLOCK) -> int:
-    return int(lib().vpa_top_tokens_workspace(Vocab(vocab, shard_width, n_shards), n_rows, block))
+    return int(lib().vpa_top_tokens_workspace(_vocab(vocab, shard_width, n_shards), n_rows, block))
 
 
+@_stream_arg
 def top_tokens(logits, vocab, shard_width, n_shards, block=DRAFT_BLOCK, workspace=None,
-               ids=None, val_bits=None, d2t=None, scale=1.0, mapped=None, stream=None):
+               ids=None, val_bits=None, d2t=None, scale=1.0, mapped=None, *, stream=None):
     """Fused get_top_tokens over all shards of each row -> (ids int32[N], val_bits int32[N]),
     plus mapped int64[N] = k + d2t[k] when a draft-to-target table is given.
 
@@ -296,29 +336,47 @@ def top_tokens(logits, vocab, shard_width, n_shards, block=DRAFT_BLOCK, workspac
     """
     ld = _logits_ld(logits)
     n = logits.shape[0]
-    need = top_tokens_workspace(vocab, shard_width, n_shards, n, block)
     dev = logits.device
+    voc = _vocab(vocab, shard_width, n_shards)
     if workspace is None:
+        need = int(lib().vpa_top_tokens_workspace(voc, n, block))
         workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=dev)
     elif not workspace.is_contiguous() or workspace.device != dev:
         raise ValueError(f"workspace must be a contiguous tensor on {dev}")
-    ids = (torch.empty(n, dtype=torch.int32, device=dev) if ids is None
-           else _out_tensor(ids, "ids", torch.int32, n, dev))
-    val_bits = (torch.empty(n, dtype=torch.int32, device=dev) if val_bits is None
-                else _out_tensor(val_bits, "val_bits", torch.int32, n, dev))
+    if ids is None and val_bits is None:
+        buf = torch.empty((2, n), dtype=torch.int32, device=dev)
+        ids, val_bits = buf[0], buf[1]
+    else:
+        ids = (torch.empty(n, dtype=torch.int32, device=dev) if ids is None
+               else _out_tensor(ids, "ids", torch.int32, n, dev))
+        val_bits = (torch.empty(n, dtype=torch.int32, device=dev) if val_bits is None
+                    else _out_tensor(val_bits, "val_bits", torch.int32, n, dev))
     if d2t is not None:
         mapped = (torch.empty(n, dtype=torch.int64, device=dev) if mapped is None
                   else _out_tensor(mapped, "mapped", torch.int64, n, dev))
-    epi, _keep = _epilogue(d2t, scale, logits.device)
-    _check(_on(logits.device, lib().vpa_top_tokens, _vp(logits), _dtype_code(logits), ld,
-               Vocab(vocab, shard_width, n_shards), n, block, _vp(workspace),
-               workspace.numel() * workspace.element_size(), epi, _vp(ids), _vp(val_bits),
-               _vp(mapped if d2t is not None else None), _stream(stream, logits.device)))
+    epi, _keep = _epilogue(d2t, scale, dev)
+    _check(_on(dev, lib().vpa_top_tokens, logits.data_ptr(), _dtype_code(logits), ld, voc, n,
+               block, workspace.data_ptr(), workspace.numel() * workspace.element_size(), epi,
+               ids.data_ptr(), val_bits.data_ptr(), _vp(mapped if d2t is not None else None),
+               _stream(stream, dev)))
     return (ids, val_bits) if d2t is None else (ids, val_bits, mapped)
 
 
+def _verify_outputs(r, k, with_targets, dev):
+    """out_tokens [r][k+1], num_sampled [r], num_rejected [r] and, if asked for,
+    target_ids [r][k+1], as views of one int32 allocation."""
+    per = r * (k + 1)
+    buf = torch.empty(per * (2 if with_targets else 1) + 2 * r, dtype=torch.int32, device=dev)
+    out_t = buf[:per].view(r, k + 1)
+    ns = buf[per:per + r]
+    nr = buf[per + r:per + 2 * r]
+    tg = buf[per + 2 * r:].view(r, k + 1) if with_targets else None
+    return out_t, ns, nr, tg
+
+
+@_stream_arg
 def greedy_verify(draft_stats, bonus_stats, draft_ids, with_targets=True, out=None,
-                  stream=None):
+                  *, stream=None):
     """Greedy verification from gathered statistics.
 
     draft_stats [S][R*K][Md][2], bonus_stats [S][R][Mb][2], draft_ids int32 [R][K].
@@ -333,11 +391,9 @@ def greedy_verify(draft_stats, bonus_stats, draft_ids, with_targets=True, out=No
     s = draft_stats.shape[0]
     if bonus_stats.shape[0] != s or draft_stats.shape[1] != r * k or bonus_stats.shape[1] != r:
         raise ValueError("statistics shapes do not match draft_ids [R][K]")
+    _same_device(dev, bonus_stats=bonus_stats)
     if out is None:
-        out_t = torch.empty((r, k + 1), dtype=torch.int32, device=dev)
-        ns = torch.empty(r, dtype=torch.int32, device=dev)
-        nr = torch.empty(r, dtype=torch.int32, device=dev)
-        tg = torch.empty((r, k + 1), dtype=torch.int32, device=dev) if with_targets else None
+        out_t, ns, nr, tg = _verify_outputs(r, k, with_targets, dev)
     else:
         out_t, ns, nr, tg = out
         for t, shape in ((out_t, (r, k + 1)), (ns, (r,)), (nr, (r,)), (tg, (r, k + 1))):
@@ -345,10 +401,9 @@ def greedy_verify(draft_stats, bonus_stats, draft_ids, with_targets=True, out=No
                                   or not t.is_contiguous()):
                 raise ValueError("preallocated verification outputs have the wrong shape/dtype")
         _same_device(dev, out_tokens=out_t, num_sampled=ns, num_rejected=nr, target_ids=tg)
-    _same_device(dev, bonus_stats=bonus_stats)
-    _check(_on(dev, lib().vpa_greedy_verify, _vp(draft_stats), draft_stats.shape[2],
-               _vp(bonus_stats), bonus_stats.shape[2], s, r, k, _vp(draft_ids), _vp(out_t), _vp(ns),
-               _vp(nr), _vp(tg), _stream(stream, dev)))
+    _check(_on(dev, lib().vpa_greedy_verify, draft_stats.data_ptr(), draft_stats.shape[2],
+               bonus_stats.data_ptr(), bonus_stats.shape[2], s, r, k, draft_ids.data_ptr(),
+               out_t.data_ptr(), ns.data_ptr(), nr.data_ptr(), _vp(tg), _stream(stream, dev)))
     return out_t, ns, nr, tg
 
 
@@ -360,36 +415,42 @@ def _total_drafts(cu, total_drafts):
     return int(cu[-1]) if total_drafts is None else int(total_drafts)
 
 
-def ragged_rows(cu, total_drafts=None, stream=None):
+@_stream_arg
+def ragged_rows(cu, total_drafts=None, *, stream=None):
     """Row lists of a ragged verification batch from cumulative draft counts
     cu [R+1]: (draft_rows int32[total_drafts], bonus_rows int32[R])."""
     total = _total_drafts(cu, total_drafts)
     n_req = cu.numel() - 1
-    draft_rows = torch.empty(total, dtype=torch.int32, device=cu.device)
-    bonus_rows = torch.empty(n_req, dtype=torch.int32, device=cu.device)
-    _check(_on(cu.device, lib().vpa_ragged_rows, _vp(cu), n_req, total, _vp(draft_rows),
-               _vp(bonus_rows), _stream(stream, cu.device)))
+    buf = torch.empty(total + n_req, dtype=torch.int32, device=cu.device)
+    draft_rows, bonus_rows = buf[:total], buf[total:]
+    _check(_on(cu.device, lib().vpa_ragged_rows, cu.data_ptr(), n_req, total,
+               draft_rows.data_ptr(), bonus_rows.data_ptr(), _stream(stream, cu.device)))
     return draft_rows, bonus_rows
 
 
+@_stream_arg
 def verify_stats_rows(logits, vocab, shard_width, n_shards, draft_rows, bonus_rows,
                       block_draft=DRAFT_BLOCK, block_bonus=BONUS_BLOCK, first_shard=0,
-                      n_local=None, stream=None):
+                      n_local=None, *, stream=None):
     """Draft- and bonus-row statistics for two explicit row lists in one launch:
     (draft_stats [n_local][len(draft_rows)][Md][2], bonus_stats [n_local][len(bonus_rows)][Mb][2])."""
     ld = _logits_ld(logits)
+    dev = logits.device
     if n_local is None:
         n_local = n_shards - first_shard
-    _int32_dev(draft_rows, "draft_rows", logits.device)
-    _int32_dev(bonus_rows, "bonus_rows", logits.device)
+    _int32_dev(draft_rows, "draft_rows", dev)
+    _int32_dev(bonus_rows, "bonus_rows", dev)
     md = stats_slots(shard_width, n_shards, block_draft)
     mb = stats_slots(shard_width, n_shards, block_bonus)
-    dst = torch.empty((n_local, draft_rows.numel(), md, 2), dtype=torch.int32, device=logits.device)
-    bst = torch.empty((n_local, bonus_rows.numel(), mb, 2), dtype=torch.int32, device=logits.device)
-    _check(_on(logits.device, lib().vpa_verify_stats_rows, _vp(logits), _dtype_code(logits), ld,
-               Vocab(vocab, shard_width, n_shards), first_shard, n_local, _vp(draft_rows),
-               draft_rows.numel(), _vp(bonus_rows), bonus_rows.numel(), logits.shape[0],
-               block_draft, block_bonus, _vp(dst), _vp(bst), _stream(stream, logits.device)))
+    nd_rows, nb_rows = draft_rows.numel(), bonus_rows.numel()
+    nd = n_local * nd_rows * md * 2
+    buf = torch.empty(nd + n_local * nb_rows * mb * 2, dtype=torch.int32, device=dev)
+    dst = buf[:nd].view(n_local, nd_rows, md, 2)
+    bst = buf[nd:].view(n_local, nb_rows, mb, 2)
+    _check(_on(dev, lib().vpa_verify_stats_rows, logits.data_ptr(), _dtype_code(logits), ld,
+               _vocab(vocab, shard_width, n_shards), first_shard, n_local, draft_rows.data_ptr(),
+               nd_rows, bonus_rows.data_ptr(), nb_rows, logits.shape[0], block_draft, block_bonus,
+               dst.data_ptr(), bst.data_ptr(), _stream(stream, dev)))
     return dst, bst
 
 
@@ -406,8 +467,9 @@ def _prefilling_flags(prefilling, n_req, device):
     return prefilling
 
 
+@_stream_arg
 def greedy_verify_ragged(draft_stats, bonus_stats, cu, draft_ids, total_drafts=None,
-                         with_targets=True, prefilling=None, stream=None):
+                         with_targets=True, prefilling=None, *, stream=None):
     """Ragged greedy verification from statistics.  cu int32 [R+1] cumulative
     draft counts; draft_ids int32 [total_drafts]; prefilling: optional bool or
     uint8 [R], true for a request still prefilling, which samples nothing (-1
@@ -426,22 +488,27 @@ def greedy_verify_ragged(draft_stats, bonus_stats, cu, draft_ids, total_drafts=N
         raise ValueError("statistics / draft_ids do not match the offsets")
     if draft_stats.shape[0] != bonus_stats.shape[0]:
         raise ValueError("draft and bonus statistics have different shard counts")
-    out = torch.empty(total + n_req, dtype=torch.int32, device=dev)
-    ns = torch.empty(n_req, dtype=torch.int32, device=dev)
-    nr = torch.empty(n_req, dtype=torch.int32, device=dev)
-    tg = torch.empty(total + n_req, dtype=torch.int32, device=dev) if with_targets else None
-    _check(_on(dev, lib().vpa_greedy_verify_ragged, _vp(draft_stats), draft_stats.shape[2],
-               _vp(bonus_stats), bonus_stats.shape[2], bonus_stats.shape[0], n_req, _vp(cu), total,
-               _vp(draft_ids), _vp(prefilling), _vp(out), _vp(ns), _vp(nr), _vp(tg),
-               _stream(stream, dev)))
+    per = total + n_req
+    buf = torch.empty(per * (2 if with_targets else 1) + 2 * n_req, dtype=torch.int32, device=dev)
+    out, ns, nr = buf[:per], buf[per:per + n_req], buf[per + n_req:per + 2 * n_req]
+    tg = buf[per + 2 * n_req:] if with_targets else None
+    _check(_on(dev, lib().vpa_greedy_verify_ragged, draft_stats.data_ptr(), draft_stats.shape[2],
+               bonus_stats.data_ptr(), bonus_stats.shape[2], bonus_stats.shape[0], n_req,
+               cu.data_ptr(), total, draft_ids.data_ptr(), _vp(prefilling), out.data_ptr(),
+               ns.data_ptr(), nr.data_ptr(), _vp(tg), _stream(stream, dev)))
     return out, ns, nr, tg
 
 
+@_stream_arg
 def verify_ragged(logits, vocab, shard_width, n_shards, cu, draft_ids, total_drafts=None,
                   block_draft=DRAFT_BLOCK, block_bonus=BONUS_BLOCK, with_targets=True,
-                  prefilling=None, stream=None):
-    """The whole ragged verification on one GPU: row lists, statistics, finish."""
+                  prefilling=None, *, stream=None):
+    """The whole ragged verification on one GPU: row lists, statistics, finish.
+    logits must hold the total_drafts + R rows the requests own."""
     total = _total_drafts(cu, total_drafts)
+    n_req = cu.numel() - 1
+    if logits.shape[0] < total + n_req:
+        raise ValueError(f"logits has {logits.shape[0]} rows, the requests own {total + n_req}")
     draft_rows, bonus_rows = ragged_rows(cu, total, stream=stream)
     dst, bst = verify_stats_rows(logits, vocab, shard_width, n_shards, draft_rows, bonus_rows,
                                  block_draft, block_bonus, stream=stream)
