@@ -38,16 +38,16 @@ def _bind(lib):
     lib.vpa_ref_block_stats.restype = None
     lib.vpa_ref_combine.argtypes = [vp, i32, i64, i32, vp, vp]
     lib.vpa_ref_combine.restype = None
-    lib.vpa_ref_greedy_verify.argtypes = [vp, i32, vp, i32, i32, i64, i32, vp, vp, vp, vp, vp]
+    lib.vpa_ref_greedy_verify.argtypes = [vp, i32, vp, i32, i32, i64, i32, vp, vp, vp, vp, vp, vp]
     lib.vpa_ref_greedy_verify.restype = None
     lib.vpa_ref_greedy_verify_logits.argtypes = [vp, ctypes.c_int, i64, i64, i64, i32, vp, vp,
-                                                 vp, vp, vp]
+                                                 vp, vp, vp, vp]
     lib.vpa_ref_greedy_verify_logits.restype = None
     lib.vpa_ref_greedy_verify_ragged.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, vp, vp,
-                                                 vp, vp, vp]
+                                                 vp, vp, vp, vp]
     lib.vpa_ref_greedy_verify_ragged.restype = None
     lib.vpa_ref_greedy_verify_ragged_stats.argtypes = [vp, i32, vp, i32, i32, i64, vp, vp, vp, vp,
-                                                       vp, vp, vp]
+                                                       vp, vp, vp, vp]
     lib.vpa_ref_greedy_verify_ragged_stats.restype = None
     lib.vpa_ref_map_ids.argtypes = [vp, i64, vp, i64, vp]
     lib.vpa_ref_map_ids.restype = None
@@ -84,6 +84,16 @@ def _flags(flags, n):
     if flags.numel() != n:
         raise ValueError(f"{flags.numel()} flags for {n} requests")
     return flags
+
+
+def _counts(accept, n):
+    """Optional synthetic accept counts as a contiguous int32 [n] tensor (None stays None)."""
+    if accept is None:
+        return None
+    accept = torch.as_tensor(accept).to("cpu").to(torch.int32).reshape(-1).contiguous()
+    if accept.numel() != n:
+        raise ValueError(f"{accept.numel()} accept counts for {n} requests")
+    return accept
 
 
 class Oracle:
@@ -136,10 +146,12 @@ class Oracle:
         return ids, vals.to(torch.int64) & 0xFFFFFFFF
 
     def greedy_verify(self, draft_stats: torch.Tensor, bonus_stats: torch.Tensor,
-                      draft_ids: torch.Tensor):
+                      draft_ids: torch.Tensor, accept=None):
         """Greedy verification from gathered statistics.
 
-        draft_stats [S][R*K][Md][2], bonus_stats [S][R][Mb][2], draft_ids int32 [R][K].
+        draft_stats [S][R*K][Md][2], bonus_stats [S][R][Mb][2], draft_ids int32 [R][K];
+        accept: optional synthetic accept counts [R] (>= 0: accept that many
+        drafts whatever they are; < 0: real acceptance).
         Returns (out_tokens [R][K+1], num_sampled [R], num_rejected [R], target_ids [R][K+1]).
         """
         draft_stats = draft_stats.contiguous()
@@ -148,39 +160,45 @@ class Oracle:
         r, k = draft_ids.shape
         s, _, md, _ = draft_stats.shape
         mb = bonus_stats.shape[2]
+        acc = _counts(accept, r)
         out, ns, nr, tg = _verify_outputs(r, k)
         if r:
             self.lib.vpa_ref_greedy_verify(_ptr(draft_stats), md, _ptr(bonus_stats), mb, s, r, k,
-                                           _ptr(draft_ids), _ptr(out), _ptr(ns), _ptr(nr),
-                                           _ptr(tg))
+                                           _ptr(draft_ids), _ptr(acc), _ptr(out), _ptr(ns),
+                                           _ptr(nr), _ptr(tg))
         return out, ns, nr, tg
 
-    def greedy_verify_logits(self, x: torch.Tensor, vocab: int, draft_ids: torch.Tensor):
-        """Greedy verification from full logits: request r owns rows r*(K+1)..r*(K+1)+K."""
+    def greedy_verify_logits(self, x: torch.Tensor, vocab: int, draft_ids: torch.Tensor,
+                             accept=None):
+        """Greedy verification from full logits: request r owns rows r*(K+1)..r*(K+1)+K;
+        accept: optional synthetic accept counts [R]."""
         ld = _check_logits(x)
         draft_ids = draft_ids.to(torch.int32).contiguous()
         r, k = draft_ids.shape
         if x.shape[0] < r * (k + 1):
             raise ValueError("logits have fewer rows than requests*(K+1)")
+        acc = _counts(accept, r)
         out, ns, nr, tg = _verify_outputs(r, k)
         if r:
             self.lib.vpa_ref_greedy_verify_logits(_ptr(x), _dtype_code(x), ld, vocab, r, k,
-                                                  _ptr(draft_ids), _ptr(out), _ptr(ns),
+                                                  _ptr(draft_ids), _ptr(acc), _ptr(out), _ptr(ns),
                                                   _ptr(nr), _ptr(tg))
         return out, ns, nr, tg
 
 
     def greedy_verify_ragged(self, x: torch.Tensor, vocab: int, cu: torch.Tensor,
-                             draft_ids: torch.Tensor, prefilling=None):
+                             draft_ids: torch.Tensor, prefilling=None, accept=None):
         """Ragged greedy verification from full logits.  cu int32 [R+1] cumulative
         draft counts; request r owns rows cu[r]+r..cu[r]+r+K_r; prefilling: optional
-        [R] flags (nonzero = still prefilling: samples nothing).  Returns
+        [R] flags (nonzero = still prefilling: samples nothing); accept: optional
+        synthetic accept counts [R] (< 0: real acceptance).  Returns
         (out_tokens [cu[R]+R], num_sampled [R], num_rejected [R], target_ids [cu[R]+R])."""
         ld = _check_logits(x)
         cu = cu.to(torch.int32).contiguous()
         draft_ids = draft_ids.to(torch.int32).contiguous()
         r = cu.numel() - 1
         pf = _flags(prefilling, r)
+        acc = _counts(accept, r)
         total = int(cu[-1]) if r > 0 else 0
         if x.shape[0] < total + r:
             raise ValueError("logits have fewer rows than drafts + requests")
@@ -190,12 +208,13 @@ class Oracle:
         tg = torch.empty(total + r, dtype=torch.int32)
         if r:
             self.lib.vpa_ref_greedy_verify_ragged(_ptr(x), _dtype_code(x), ld, vocab, r, _ptr(cu),
-                                                  _ptr(draft_ids), _ptr(pf), _ptr(out), _ptr(ns),
-                                                  _ptr(nr), _ptr(tg))
+                                                  _ptr(draft_ids), _ptr(pf), _ptr(acc), _ptr(out),
+                                                  _ptr(ns), _ptr(nr), _ptr(tg))
         return out, ns, nr, tg
 
     def greedy_verify_ragged_stats(self, draft_stats: torch.Tensor, bonus_stats: torch.Tensor,
-                                   cu: torch.Tensor, draft_ids: torch.Tensor, prefilling=None):
+                                   cu: torch.Tensor, draft_ids: torch.Tensor, prefilling=None,
+                                   accept=None):
         """Ragged greedy verification from statistics [S][cu[R]][Md][2], [S][R][Mb][2]."""
         draft_stats = draft_stats.contiguous()
         bonus_stats = bonus_stats.contiguous()
@@ -203,6 +222,7 @@ class Oracle:
         draft_ids = draft_ids.to(torch.int32).contiguous()
         r = cu.numel() - 1
         pf = _flags(prefilling, r)
+        acc = _counts(accept, r)
         total = int(cu[-1]) if r > 0 else 0
         s, md, mb = draft_stats.shape[0], draft_stats.shape[2], bonus_stats.shape[2]
         out = torch.empty(total + r, dtype=torch.int32)
@@ -212,8 +232,8 @@ class Oracle:
         if r:
             self.lib.vpa_ref_greedy_verify_ragged_stats(_ptr(draft_stats), md, _ptr(bonus_stats),
                                                         mb, s, r, _ptr(cu), _ptr(draft_ids),
-                                                        _ptr(pf), _ptr(out), _ptr(ns), _ptr(nr),
-                                                        _ptr(tg))
+                                                        _ptr(pf), _ptr(acc), _ptr(out), _ptr(ns),
+                                                        _ptr(nr), _ptr(tg))
         return out, ns, nr, tg
 
     def map_ids(self, ids: torch.Tensor, d2t: torch.Tensor):

@@ -57,6 +57,14 @@
  *    still prefilling samples nothing, so all K_r+1 of its output slots
  *    hold -1 and sampled = rejected = 0; its target tokens are still
  *    reported.
+ *  - synthetic acceptance ([P4] "Purpose" item 1 names it beside the real
+ *    acceptance, and "Test Plan" lists it among the verified cases, with no
+ *    rule; the reading taken here): the caller may give each request an
+ *    accept count a_r.  With a_r >= 0 the first min(a_r, K_r) drafts are
+ *    accepted whatever their values (random draws behind a_r are the
+ *    caller's); the next position emits its target token as usual; a_r < 0,
+ *    or no counts at all, means the real greedy rule.  A prefilling request
+ *    still samples nothing.
  *  - optional epilogue of the combined argmax k:
  *    [P2] PR #39419 "[SpecDecode] Reduce TP communication for large-vocab
  *    draft models speculative decoding", note "Refactor local argmax code":
@@ -227,15 +235,21 @@ void vpa_ref_combine(const ref_stat *stats, int32_t n_shards, int64_t n_rows, in
     }
 }
 
-/* Greedy acceptance for one request ([P4] item 1) given the K+1 target
- * tokens: the drafts are accepted while they equal the target token; the
- * first position that differs (or the bonus position) emits the target. */
-static void ref_accept(const int32_t *draft, const int32_t *target, int32_t k, int32_t *out,
-                       int32_t *n_sampled, int32_t *n_rejected)
+/* Acceptance for one request ([P4] item 1) given the K+1 target tokens.
+ * Real acceptance (synth < 0): the drafts are accepted while they equal the
+ * target token.  Synthetic acceptance (synth >= 0): the first min(synth, K)
+ * drafts are accepted whatever their values.  The position after the
+ * accepted ones (the bonus position when all K are accepted) emits its
+ * target token. */
+static void ref_accept(const int32_t *draft, const int32_t *target, int32_t k, int32_t synth,
+                       int32_t *out, int32_t *n_sampled, int32_t *n_rejected)
 {
     int32_t n = 0;
-    while (n < k && draft[n] == target[n])
-        ++n;
+    if (synth >= 0)
+        n = synth < k ? synth : k;
+    else
+        while (n < k && draft[n] == target[n])
+            ++n;
     for (int32_t j = 0; j <= k; ++j)
         out[j] = j < n ? draft[j] : (j == n ? target[j] : -1);
     *n_sampled = n + 1;
@@ -252,21 +266,29 @@ static void ref_prefilling(int32_t k, int32_t *out, int32_t *n_sampled, int32_t 
     *n_rejected = 0;
 }
 
+/* Synthetic accept count of request r: accept[r], or -1 (real acceptance)
+ * when no counts are given. */
+static int32_t ref_synth(const int32_t *accept, int64_t r)
+{
+    return accept ? accept[r] : -1;
+}
+
 /* Greedy verification from gathered statistics: draft stats
  * [S][R*K][m_draft] (row i = request i/K, position i%K) and bonus stats
- * [S][R][m_bonus].  target_ids may be NULL. */
+ * [S][R][m_bonus].  accept (synthetic accept counts, [R]) and target_ids may
+ * be NULL. */
 void vpa_ref_greedy_verify(const ref_stat *draft_stats, int32_t m_draft, const ref_stat *bonus_stats,
                            int32_t m_bonus, int32_t n_shards, int64_t n_req, int32_t k,
-                           const int32_t *draft_ids, int32_t *out_tokens, int32_t *num_sampled,
-                           int32_t *num_rejected, int32_t *target_ids)
+                           const int32_t *draft_ids, const int32_t *accept, int32_t *out_tokens,
+                           int32_t *num_sampled, int32_t *num_rejected, int32_t *target_ids)
 {
     int32_t tgt[k + 1];
     for (int64_t r = 0; r < n_req; ++r) {
         for (int32_t j = 0; j < k; ++j)
             tgt[j] = ref_combine_row(draft_stats, n_shards, n_req * k, r * k + j, m_draft).id;
         tgt[k] = ref_combine_row(bonus_stats, n_shards, n_req, r, m_bonus).id;
-        ref_accept(draft_ids + r * k, tgt, k, out_tokens + r * (k + 1), num_sampled + r,
-                   num_rejected + r);
+        ref_accept(draft_ids + r * k, tgt, k, ref_synth(accept, r), out_tokens + r * (k + 1),
+                   num_sampled + r, num_rejected + r);
         if (target_ids)
             for (int32_t j = 0; j <= k; ++j)
                 target_ids[r * (k + 1) + j] = tgt[j];
@@ -277,8 +299,9 @@ void vpa_ref_greedy_verify(const ref_stat *draft_stats, int32_t m_draft, const r
  * r*(K+1) .. r*(K+1)+K (K draft positions, then the bonus position), and the
  * target token of each row is its full-row argmax. */
 void vpa_ref_greedy_verify_logits(const void *x, int dtype, int64_t ld, int64_t vocab, int64_t n_req,
-                                  int32_t k, const int32_t *draft_ids, int32_t *out_tokens,
-                                  int32_t *num_sampled, int32_t *num_rejected, int32_t *target_ids)
+                                  int32_t k, const int32_t *draft_ids, const int32_t *accept,
+                                  int32_t *out_tokens, int32_t *num_sampled, int32_t *num_rejected,
+                                  int32_t *target_ids)
 {
     int32_t tgt[k + 1];
     uint32_t vb;
@@ -287,8 +310,8 @@ void vpa_ref_greedy_verify_logits(const void *x, int dtype, int64_t ld, int64_t 
             const char *row = (const char *)x + (dtype == REF_BF16 ? 2 : 4) * (r * (k + 1) + j) * ld;
             vpa_ref_argmax(row, dtype, ld, 1, vocab, &tgt[j], &vb);
         }
-        ref_accept(draft_ids + r * k, tgt, k, out_tokens + r * (k + 1), num_sampled + r,
-                   num_rejected + r);
+        ref_accept(draft_ids + r * k, tgt, k, ref_synth(accept, r), out_tokens + r * (k + 1),
+                   num_sampled + r, num_rejected + r);
         if (target_ids)
             for (int32_t j = 0; j <= k; ++j)
                 target_ids[r * (k + 1) + j] = tgt[j];
@@ -322,11 +345,13 @@ uint32_t vpa_ref_scale_bits(uint32_t bits, float scale)
  * cu[r]+r .. cu[r]+r+K_r (K_r = cu[r+1]-cu[r] drafts, then the bonus row);
  * draft_ids holds the cu[R] drafts back to back; out_tokens and target_ids
  * hold K_r+1 entries per request at offset cu[r]+r.  prefilling (NULL = none)
- * flags the requests that are still prefilling. */
+ * flags the requests that are still prefilling; accept (NULL = none) holds
+ * synthetic accept counts. */
 void vpa_ref_greedy_verify_ragged(const void *x, int dtype, int64_t ld, int64_t vocab, int64_t n_req,
                                   const int32_t *cu, const int32_t *draft_ids,
-                                  const uint8_t *prefilling, int32_t *out_tokens,
-                                  int32_t *num_sampled, int32_t *num_rejected, int32_t *target_ids)
+                                  const uint8_t *prefilling, const int32_t *accept,
+                                  int32_t *out_tokens, int32_t *num_sampled,
+                                  int32_t *num_rejected, int32_t *target_ids)
 {
     for (int64_t r = 0; r < n_req; ++r) {
         int32_t k = cu[r + 1] - cu[r];
@@ -340,8 +365,8 @@ void vpa_ref_greedy_verify_ragged(const void *x, int dtype, int64_t ld, int64_t 
         if (prefilling && prefilling[r])
             ref_prefilling(k, out_tokens + base, num_sampled + r, num_rejected + r);
         else
-            ref_accept(draft_ids + cu[r], tgt, k, out_tokens + base, num_sampled + r,
-                       num_rejected + r);
+            ref_accept(draft_ids + cu[r], tgt, k, ref_synth(accept, r), out_tokens + base,
+                       num_sampled + r, num_rejected + r);
         if (target_ids)
             for (int32_t j = 0; j <= k; ++j)
                 target_ids[base + j] = tgt[j];
@@ -355,8 +380,9 @@ void vpa_ref_greedy_verify_ragged_stats(const ref_stat *draft_stats, int32_t m_d
                                         const ref_stat *bonus_stats, int32_t m_bonus,
                                         int32_t n_shards, int64_t n_req, const int32_t *cu,
                                         const int32_t *draft_ids, const uint8_t *prefilling,
-                                        int32_t *out_tokens, int32_t *num_sampled,
-                                        int32_t *num_rejected, int32_t *target_ids)
+                                        const int32_t *accept, int32_t *out_tokens,
+                                        int32_t *num_sampled, int32_t *num_rejected,
+                                        int32_t *target_ids)
 {
     int64_t total = cu[n_req];
     for (int64_t r = 0; r < n_req; ++r) {
@@ -369,8 +395,8 @@ void vpa_ref_greedy_verify_ragged_stats(const ref_stat *draft_stats, int32_t m_d
         if (prefilling && prefilling[r])
             ref_prefilling(k, out_tokens + base, num_sampled + r, num_rejected + r);
         else
-            ref_accept(draft_ids + cu[r], tgt, k, out_tokens + base, num_sampled + r,
-                       num_rejected + r);
+            ref_accept(draft_ids + cu[r], tgt, k, ref_synth(accept, r), out_tokens + base,
+                       num_sampled + r, num_rejected + r);
         if (target_ids)
             for (int32_t j = 0; j <= k; ++j)
                 target_ids[base + j] = tgt[j];

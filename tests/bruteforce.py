@@ -10,6 +10,9 @@ oracle so that the two pin each other.
   slot ranges derived from the shard start.
 * greedy verification: the accepted prefix is the longest run of equal
   (draft, target) pairs from the left (itertools.takewhile).
+* synthetic acceptance: the emitted tokens are the list of accepted drafts
+  with the next target appended, padded with -1 to K+1 entries; the counts
+  are read off that list.
 
 The rule itself (vLLM PR #62604, "Purpose" items 1 and 2): NaN beats every
 number, ties go to the lowest id, -0 equals +0; blocks keep global
@@ -78,3 +81,15 @@ def bf_verify(targets, drafts):
     n = len(list(itertools.takewhile(lambda p: p[0] == p[1], zip(drafts, targets))))
     out = list(drafts[:n]) + [targets[n]] + [-1] * (k - n)
     return out, n + 1, k - n
+
+
+def bf_verify_synthetic(targets, drafts, accept):
+    """(out_tokens, sampled, rejected) for one request under an accept count:
+    accept < 0 is the real greedy rule; otherwise the first accept drafts
+    (at most K) are taken as they are, followed by the next target."""
+    if accept < 0:
+        return bf_verify(targets, drafts)
+    k = len(drafts)
+    taken = list(drafts[:accept])
+    emitted = taken + [targets[len(taken)]]
+    return emitted + [-1] * (k + 1 - len(emitted)), len(emitted), k - len(taken)

@@ -86,3 +86,16 @@ def ragged_verify_cases():
         assert len(fields) == 7, line
         out.append(tuple(fields))
     return out
+
+
+def synthetic_verify_cases():
+    """[(cu, targets, drafts, accept, out_tokens, sampled, rejected, prefilling)]
+    as int lists; prefilling is None where a case gives no flags."""
+    out = []
+    for line in _lines("synthetic_verify_cases.txt"):
+        fields = [[int(t) for t in p.split()] for p in line.split("|")]
+        if len(fields) == 7:
+            fields.append(None)
+        assert len(fields) == 8, line
+        out.append(tuple(fields))
+    return out

@@ -15,7 +15,11 @@ oracle disagrees with
   * the greedy acceptance rule, by brute force over every draft tuple of tiny
     vocabularies;
   * the epilogue of the combined argmax (draft-to-target map, positive scale)
-    against hand-worked cases and torch's fp32 multiply.
+    against hand-worked cases and torch's fp32 multiply;
+  * synthetic acceptance (caller-given accept counts) against hand-worked
+    cases, brute force over every draft tuple and count, and the invariants
+    that a count equal to the real accepted length, or no count at all,
+    changes nothing.
 The same pins run against deliberately broken copies of the oracle
 (tests/test_oracle_mutants.py) to show that each plausible mistake is caught.
 """
@@ -300,7 +304,99 @@ def pin_ragged_verify(o):
                                int(plain[2][r])), (cu, r, pf)
 
 
+def _uniform_stats(o, x, vocab, n_req, k):
+    """Draft and bonus statistics of a uniform batch (one shard, one-column blocks)."""
+    draft_rows, bonus_rows = _verify_rows(n_req, k)
+    return (o.block_stats(x, vocab, vocab, 1, 1, rows=draft_rows),
+            o.block_stats(x, vocab, vocab, 1, 1, rows=bonus_rows))
+
+
+def pin_synthetic_verify(o):
+    """Synthetic acceptance: hand-worked cases through all four verification
+    entry points; brute force over every target tuple, draft tuple in
+    {-1..V-1}^K and count in {-2..K+1} (V <= 2, K <= 3); a count equal to the
+    real accepted length reproduces the real outputs; counts that are all
+    negative equal giving none; random ragged batches with counts and
+    prefilling flags, request by request."""
+    import oracle as _oracle
+    for cu, targets, drafts, acc, out, ns, nr, pf in golden_io.synthetic_verify_cases():
+        x = _ragged_logits(targets, 16)
+        cu_t = torch.tensor(cu, dtype=torch.int32)
+        d = torch.tensor(drafts, dtype=torch.int32)
+        got = o.greedy_verify_ragged(x, 16, cu_t, d, prefilling=pf, accept=acc)
+        assert (got[0].tolist(), got[1].tolist(), got[2].tolist()) == (out, ns, nr), \
+            (cu, acc, pf, got)
+        assert got[3].tolist() == targets
+        draft_rows, bonus_rows = _oracle.ragged_rows(cu_t)
+        dst = o.block_stats(x, 16, 16, 1, 1, rows=draft_rows)
+        bst = o.block_stats(x, 16, 16, 1, 1, rows=bonus_rows)
+        got2 = o.greedy_verify_ragged_stats(dst, bst, cu_t, d, prefilling=pf, accept=acc)
+        for a, b in zip(got, got2):
+            assert torch.equal(a, b), (cu, acc)
+        ks = {cu[r + 1] - cu[r] for r in range(len(cu) - 1)}
+        if pf is None and len(ks) == 1 and min(ks) > 0:
+            k, n_req = ks.pop(), len(cu) - 1
+            du = d.reshape(n_req, k)
+            got3 = o.greedy_verify_logits(x, 16, du, accept=acc)
+            got4 = o.greedy_verify(*_uniform_stats(o, x, 16, n_req, k), du, accept=acc)
+            for g in (got3, got4):
+                assert g[0].reshape(-1).tolist() == out and g[1].tolist() == ns \
+                    and g[2].tolist() == nr, (cu, acc, g)
+    for vocab in (1, 2):
+        for k in (1, 2, 3):
+            for targets in itertools.product(range(vocab), repeat=k + 1):
+                x = torch.zeros((k + 1, vocab), dtype=torch.float32)
+                for j, t in enumerate(targets):
+                    x[j, t] = 1.0
+                cases = [(dr, a) for dr in itertools.product(range(-1, vocab), repeat=k)
+                         for a in range(-2, k + 2)]
+                n_req = len(cases)
+                xx = x.repeat(n_req, 1)
+                d = torch.tensor([c[0] for c in cases], dtype=torch.int32)
+                acc = [c[1] for c in cases]
+                got = o.greedy_verify_logits(xx, vocab, d, accept=acc)
+                got2 = o.greedy_verify(*_uniform_stats(o, xx, vocab, n_req, k), d, accept=acc)
+                real = o.greedy_verify_logits(xx, vocab, d)
+                same = o.greedy_verify_logits(xx, vocab, d, accept=real[1] - 1)
+                for r, (dr, a) in enumerate(cases):
+                    want = bf.bf_verify_synthetic(list(targets), list(dr), a)
+                    for g in (got, got2):
+                        assert (g[0][r].tolist(), int(g[1][r]), int(g[2][r])) == want, \
+                            (vocab, k, targets, dr, a, want)
+                for a, b in zip(same, real):
+                    assert torch.equal(a, b), (vocab, k, targets)
+                none = o.greedy_verify_logits(xx, vocab, d, accept=[-1] * n_req)
+                for a, b in zip(none, real):
+                    assert torch.equal(a, b), (vocab, k, targets)
+    rng = random.Random(7)
+    for trial in range(200):
+        vocab = rng.randint(1, 4)
+        n_req = rng.randint(1, 6)
+        ks = [rng.randint(0, 4) for _ in range(n_req)]
+        cu = [0]
+        for k in ks:
+            cu.append(cu[-1] + k)
+        targets = [rng.randrange(vocab) for _ in range(cu[-1] + n_req)]
+        drafts = [rng.randint(-1, vocab - 1) for _ in range(cu[-1])]
+        acc = [rng.randint(-2, 5) for _ in range(n_req)]
+        pf = [int(rng.random() < 0.3) for _ in range(n_req)] if trial % 2 else None
+        x = _ragged_logits(targets, vocab)
+        cu_t = torch.tensor(cu, dtype=torch.int32)
+        d = torch.tensor(drafts, dtype=torch.int32)
+        out, ns, nr, tg = o.greedy_verify_ragged(x, vocab, cu_t, d, prefilling=pf, accept=acc)
+        assert tg.tolist() == targets
+        for r, k in enumerate(ks):
+            base = cu[r] + r
+            got = (out[base:base + k + 1].tolist(), int(ns[r]), int(nr[r]))
+            if pf and pf[r]:
+                assert got == ([-1] * (k + 1), 0, 0), (cu, r, acc, got)
+                continue
+            want = bf.bf_verify_synthetic(targets[base:base + k + 1], drafts[cu[r]:cu[r] + k],
+                                          acc[r])
+            assert got == want, (cu, r, acc, got, want)
+
+
 ALL_PINS = [pin_golden_argmax, pin_golden_block_stats, pin_golden_verify, pin_exhaustive_argmax,
             pin_torch_argmax, pin_slots, pin_block_stats_bruteforce, pin_invariance,
             pin_verify_bruteforce, pin_golden_epilogue, pin_scale_matches_torch,
-            pin_ragged_verify]
+            pin_ragged_verify, pin_synthetic_verify]

@@ -43,8 +43,8 @@ MUTANTS = [
      "            if (ref_better(ref_value(st.val_bits), st.id, ref_value(best.val_bits), best.id))\n                best = st;\n        }\n    return best;",
      "            if (ref_value(st.val_bits) > ref_value(best.val_bits))\n                best = st;\n        }\n    return best;"),
     ("accept_counts_all_matches",
-     "    while (n < k && draft[n] == target[n])\n        ++n;",
-     "    for (int32_t q = 0; q < k; ++q)\n        n += draft[q] == target[q];"),
+     "        while (n < k && draft[n] == target[n])\n            ++n;",
+     "        for (int32_t q = 0; q < k; ++q)\n            n += draft[q] == target[q];"),
     ("correction_is_draft",
      "        out[j] = j < n ? draft[j] : (j == n ? target[j] : -1);",
      "        out[j] = j < n ? draft[j] : (j == n ? (j < k ? draft[j] : target[j]) : -1);"),
@@ -64,8 +64,8 @@ MUTANTS = [
     ("prefilling_rejects_its_drafts",
      "    *n_sampled = 0;\n    *n_rejected = 0;", "    *n_sampled = 0;\n    *n_rejected = k;"),
     ("prefilling_flag_of_next_request",
-     "        if (prefilling && prefilling[r])\n            ref_prefilling(k, out_tokens + base, num_sampled + r, num_rejected + r);\n        else\n            ref_accept(draft_ids + cu[r], tgt, k, out_tokens + base, num_sampled + r,\n                       num_rejected + r);\n        if (target_ids)\n            for (int32_t j = 0; j <= k; ++j)\n                target_ids[base + j] = tgt[j];\n    }\n}\n\n/* Ragged greedy verification from gathered",
-     "        if (prefilling && prefilling[r + 1 < n_req ? r + 1 : r])\n            ref_prefilling(k, out_tokens + base, num_sampled + r, num_rejected + r);\n        else\n            ref_accept(draft_ids + cu[r], tgt, k, out_tokens + base, num_sampled + r,\n                       num_rejected + r);\n        if (target_ids)\n            for (int32_t j = 0; j <= k; ++j)\n                target_ids[base + j] = tgt[j];\n    }\n}\n\n/* Ragged greedy verification from gathered"),
+     "        if (prefilling && prefilling[r])\n            ref_prefilling(k, out_tokens + base, num_sampled + r, num_rejected + r);\n        else\n            ref_accept(draft_ids + cu[r], tgt, k, ref_synth(accept, r), out_tokens + base,\n                       num_sampled + r, num_rejected + r);\n        if (target_ids)\n            for (int32_t j = 0; j <= k; ++j)\n                target_ids[base + j] = tgt[j];\n    }\n}\n\n/* Ragged greedy verification from gathered",
+     "        if (prefilling && prefilling[r + 1 < n_req ? r + 1 : r])\n            ref_prefilling(k, out_tokens + base, num_sampled + r, num_rejected + r);\n        else\n            ref_accept(draft_ids + cu[r], tgt, k, ref_synth(accept, r), out_tokens + base,\n                       num_sampled + r, num_rejected + r);\n        if (target_ids)\n            for (int32_t j = 0; j <= k; ++j)\n                target_ids[base + j] = tgt[j];\n    }\n}\n\n/* Ragged greedy verification from gathered"),
     ("map_without_draft_id",
      "? (int64_t)ids[i] + d2t[ids[i]] : -1;", "? d2t[ids[i]] : -1;"),
     ("nan_scaled_too",
@@ -76,6 +76,22 @@ MUTANTS = [
     ("bonus_from_last_draft_row",
      "r * k + j, m_draft).id;\n        tgt[k] = ref_combine_row(bonus_stats, n_shards, n_req, r, m_bonus).id;",
      "r * k + j, m_draft).id;\n        tgt[k] = tgt[k - 1];"),
+    ("synthetic_counts_ignored",
+     "    return accept ? accept[r] : -1;", "    (void)accept;\n    (void)r;\n    return -1;"),
+    ("synthetic_count_of_previous_request",
+     "    return accept ? accept[r] : -1;", "    return accept ? accept[r > 0 ? r - 1 : 0] : -1;"),
+    ("synthetic_capped_below_k",
+     "        n = synth < k ? synth : k;", "        n = synth < k ? synth : k - 1;"),
+    ("synthetic_off_by_one",
+     "        n = synth < k ? synth : k;", "        n = synth + 1 < k ? synth + 1 : k;"),
+    ("synthetic_stops_at_first_mismatch",
+     "        n = synth < k ? synth : k;",
+     "        while (n < synth && n < k && draft[n] == target[n])\n            ++n;"),
+    ("negative_count_is_synthetic",
+     "    if (synth >= 0)\n", "    if (synth >= -1)\n"),
+    ("prefilling_yields_to_synthetic",
+     "            vpa_ref_argmax(row, dtype, ld, 1, vocab, &tgt[j], &vb);\n        }\n        if (prefilling && prefilling[r])",
+     "            vpa_ref_argmax(row, dtype, ld, 1, vocab, &tgt[j], &vb);\n        }\n        if (prefilling && prefilling[r] && !accept)"),
 ]
 
 
