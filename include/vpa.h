@@ -31,9 +31,9 @@
  *
  * Conventions shared by every call:
  *  - Pointers named logits, stats, ids, val_bits, mapped, d2t, draft_ids,
- *    out_tokens, num_sampled, num_rejected, target_ids, rows, draft_rows,
- *    bonus_rows, cu, prefilling and workspace are DEVICE memory owned by the
- *    caller.  The library never allocates or frees.
+ *    accept, out_tokens, num_sampled, num_rejected, target_ids, rows,
+ *    draft_rows, bonus_rows, cu, prefilling and workspace are DEVICE memory
+ *    owned by the caller.  The library never allocates or frees.
  *  - Every call only enqueues work on `stream` (a hipStream_t passed as
  *    void*; NULL is the default stream) and returns without synchronising;
  *    outputs are defined once the stream reaches that point.
@@ -223,6 +223,14 @@ vpa_status vpa_top_tokens(const void* logits, vpa_dtype dtype, int64_t ld, vpa_v
  *               (the layout vpa_verify_stats writes).
  *  draft_ids    int32 [n_req][K]; any value is legal, -1 marks a placeholder,
  *               and only a value equal to the target token is accepted.
+ *  accept       device int32 [n_req], or NULL: synthetic accept counts.  The
+ *               same "Purpose" item names synthetic acceptance beside the
+ *               real one, and "Test Plan" lists it among the verified cases,
+ *               without a rule; the reading here: with accept[r] >= 0 the
+ *               first min(accept[r], K) drafts of request r are accepted
+ *               whatever their values, and the next position emits its
+ *               target token as above; accept[r] < 0 (or NULL) is the real
+ *               rule.  Random draws behind the counts are the caller's.
  *  out_tokens   out, int32 [n_req][K+1].
  *  num_sampled  out, int32 [n_req]: accepted + 1.
  *  num_rejected out, int32 [n_req]: K - accepted.
@@ -232,8 +240,8 @@ vpa_status vpa_top_tokens(const void* logits, vpa_dtype dtype, int64_t ld, vpa_v
 vpa_status vpa_greedy_verify(const vpa_stat* draft_stats, int32_t m_draft,
                              const vpa_stat* bonus_stats, int32_t m_bonus, int32_t n_shards,
                              int64_t n_req, int32_t k, const int32_t* draft_ids,
-                             int32_t* out_tokens, int32_t* num_sampled, int32_t* num_rejected,
-                             int32_t* target_ids, void* stream);
+                             const int32_t* accept, int32_t* out_tokens, int32_t* num_sampled,
+                             int32_t* num_rejected, int32_t* target_ids, void* stream);
 
 /* Ragged greedy verification from gathered statistics: as
  * vpa_greedy_verify with a draft count per request.
@@ -245,8 +253,10 @@ vpa_status vpa_greedy_verify(const vpa_stat* draft_stats, int32_t m_draft,
  *               a request that is still prefilling.  The PR's "Test Plan"
  *               lists such requests without a rule; the reading here is that
  *               one samples nothing: all K_r+1 of its out_tokens hold -1 and
- *               num_sampled = num_rejected = 0.  Its target_ids are written
- *               as for any request.
+ *               num_sampled = num_rejected = 0, whatever its accept count.
+ *               Its target_ids are written as for any request.
+ *  accept       device int32 [n_req], or NULL: synthetic accept counts as for
+ *               vpa_greedy_verify, with K_r in place of K.
  *  out_tokens   out, int32 [total_drafts + n_req]: request r's K_r+1 entries
  *               at cu[r]+r (accepted drafts, then the correction or bonus
  *               token, then -1); a request with K_r = 0 emits its bonus token.
@@ -262,9 +272,9 @@ vpa_status vpa_greedy_verify_ragged(const vpa_stat* draft_stats, int32_t m_draft
                                     const vpa_stat* bonus_stats, int32_t m_bonus,
                                     int32_t n_shards, int64_t n_req, const int32_t* cu,
                                     int64_t total_drafts, const int32_t* draft_ids,
-                                    const uint8_t* prefilling, int32_t* out_tokens,
-                                    int32_t* num_sampled, int32_t* num_rejected,
-                                    int32_t* target_ids, void* stream);
+                                    const uint8_t* prefilling, const int32_t* accept,
+                                    int32_t* out_tokens, int32_t* num_sampled,
+                                    int32_t* num_rejected, int32_t* target_ids, void* stream);
 
 /* Message describing the last non-OK status returned on the calling thread
  * ("" if none).  The pointer stays valid until the next call on that thread. */

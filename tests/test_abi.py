@@ -107,7 +107,7 @@ def test_empty_batches_are_noops(lib):
                               None, None, None, None) == vpa.VPA_OK
     assert lib.vpa_verify_stats(FAKE, vpa.VPA_F32, 1000, V(1000, 125, 8), 0, 8, 0, 3, 8192, 1024,
                                 None, None, None) == vpa.VPA_OK
-    assert lib.vpa_greedy_verify(None, 1, None, 1, 8, 0, 3, None, None, None, None, None,
+    assert lib.vpa_greedy_verify(None, 1, None, 1, 8, 0, 3, None, None, None, None, None, None,
                                  None) == vpa.VPA_OK
 
 
@@ -182,13 +182,15 @@ def test_verify_rejects(lib):
     assert lib.vpa_verify_stats(FAKE, vpa.VPA_BF16, 200064, voc, 0, 4, 24, 4097, 8192, 1024, FAKE,
                                 FAKE, None) == vpa.VPA_ERR_INVALID
     gv = lib.vpa_greedy_verify
-    assert gv(FAKE, 7, FAKE, 50, 4, 24, 4097, FAKE, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
-    assert gv(FAKE, 7, FAKE, 50, 4, 24, 0, FAKE, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
-    assert gv(FAKE, 0, FAKE, 50, 4, 24, 3, FAKE, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
-    assert gv(FAKE, 7, FAKE, 50, 0, 24, 3, FAKE, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
-    assert gv(FAKE, 7, FAKE, 50, 4, 24, 3, None, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
-    assert gv(FAKE, 7, FAKE, 50, 4, 24, 3, FAKE, FAKE, FAKE, FAKE, FAKE_ODD, None) == vpa.VPA_ERR_INVALID
-    assert gv(FAKE, 7, FAKE, 50, 4, -1, 3, FAKE, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert gv(FAKE, 7, FAKE, 50, 4, 24, 4097, FAKE, None, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert gv(FAKE, 7, FAKE, 50, 4, 24, 0, FAKE, None, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert gv(FAKE, 0, FAKE, 50, 4, 24, 3, FAKE, None, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert gv(FAKE, 7, FAKE, 50, 0, 24, 3, FAKE, None, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert gv(FAKE, 7, FAKE, 50, 4, 24, 3, None, None, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert gv(FAKE, 7, FAKE, 50, 4, 24, 3, FAKE, None, FAKE, FAKE, FAKE, FAKE_ODD, None) == vpa.VPA_ERR_INVALID
+    assert gv(FAKE, 7, FAKE, 50, 4, -1, 3, FAKE, None, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    # synthetic accept counts must be 4-byte aligned
+    assert gv(FAKE, 7, FAKE, 50, 4, 24, 3, FAKE, FAKE_ODD, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
 
 
 def test_last_error_is_per_call_message(lib):
@@ -217,12 +219,13 @@ def test_ragged_rejects(lib):
     assert rr(FAKE_ODD, 3, 4, FAKE, FAKE, None) == vpa.VPA_ERR_INVALID
     assert rr(None, 0, 0, None, None, None) == vpa.VPA_OK
     gr = lib.vpa_greedy_verify_ragged
-    assert gr(FAKE, 0, FAKE, 50, 4, 3, FAKE, 6, FAKE, None, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
-    assert gr(FAKE, 7, FAKE, 50, 4, 3, None, 6, FAKE, None, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
-    assert gr(FAKE, 7, FAKE, 50, 4, 3, FAKE, 6, None, None, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
-    assert gr(FAKE, 7, FAKE, 50, 4, 3, FAKE, 6, FAKE, None, FAKE, FAKE, FAKE, FAKE_ODD, None) == vpa.VPA_ERR_INVALID
-    assert gr(FAKE, 7, FAKE, 50, 4, -2, FAKE, 6, FAKE, None, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
-    assert gr(None, 7, None, 50, 4, 0, None, 0, None, None, None, None, None, None, None) == vpa.VPA_OK
+    assert gr(FAKE, 0, FAKE, 50, 4, 3, FAKE, 6, FAKE, None, None, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert gr(FAKE, 7, FAKE, 50, 4, 3, None, 6, FAKE, None, None, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert gr(FAKE, 7, FAKE, 50, 4, 3, FAKE, 6, None, None, None, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert gr(FAKE, 7, FAKE, 50, 4, 3, FAKE, 6, FAKE, None, None, FAKE, FAKE, FAKE, FAKE_ODD, None) == vpa.VPA_ERR_INVALID
+    assert gr(FAKE, 7, FAKE, 50, 4, -2, FAKE, 6, FAKE, None, None, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert gr(FAKE, 7, FAKE, 50, 4, 3, FAKE, 6, FAKE, None, FAKE_ODD, FAKE, FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert gr(None, 7, None, 50, 4, 0, None, 0, None, None, None, None, None, None, None, None) == vpa.VPA_OK
 
 
 def test_launches_beyond_one_dispatch_are_rejected(lib):
@@ -242,12 +245,12 @@ def test_launches_beyond_one_dispatch_are_rejected(lib):
                                 16384, 16384, FAKE, FAKE, None) == vpa.VPA_ERR_INVALID
     assert "dispatch" in vpa.last_error()
     req = (1 << 22) + 1                          # 16 wavefronts per request at K=15
-    assert lib.vpa_greedy_verify(FAKE, 1, FAKE, 1, 1, req, 15, FAKE, FAKE, FAKE, FAKE, None,
+    assert lib.vpa_greedy_verify(FAKE, 1, FAKE, 1, 1, req, 15, FAKE, None, FAKE, FAKE, FAKE, None,
                                  None) == vpa.VPA_ERR_INVALID
     assert "dispatch" in vpa.last_error()
     req = (1 << 24) + 1                          # one 256-thread workgroup per request
-    assert lib.vpa_greedy_verify_ragged(FAKE, 1, FAKE, 1, 1, req, FAKE, 0, None, None, FAKE, FAKE,
-                                        FAKE, None, None) == vpa.VPA_ERR_INVALID
+    assert lib.vpa_greedy_verify_ragged(FAKE, 1, FAKE, 1, 1, req, FAKE, 0, None, None, None, FAKE,
+                                        FAKE, FAKE, None, None) == vpa.VPA_ERR_INVALID
     assert "dispatch" in vpa.last_error()
 
 

@@ -94,6 +94,15 @@ def _verify_both(x_cpu, vocab, w, s, n_req, k, drafts, bd, bb, name):
         assert_same(g, wv, f"{name} (no target_ids)")
     # block_stats with explicit row lists gives the same statistics
     assert_same(vpa.block_stats(x, vocab, w, s, bd, rows=_dev(draft_rows)), want_d, f"{name} rows")
+    # synthetic acceptance: per-request counts (some -1, i.e. real acceptance)
+    acc = workloads.synthetic_counts(n_req, k, seed=131 * n_req + k)
+    want_s = oracle.greedy_verify(want_d, want_b, drafts, accept=acc)
+    for a, b in zip(want_s, oracle.greedy_verify_logits(x_cpu, vocab, drafts, accept=acc)):
+        assert torch.equal(a, b)
+    got_s = vpa.greedy_verify(dst, bst, _dev(drafts), accept=_dev(acc))
+    for g, wv, nm in zip(got_s, want_s, ("out_tokens", "num_sampled", "num_rejected",
+                                         "target_ids")):
+        assert_same(g, wv, f"{name} synthetic {nm}")
     return want
 
 
@@ -165,6 +174,16 @@ def test_verify_at_the_draft_limit():
                                         "target_ids")):
         assert_same(a, b, f"ragged draft limit {nm}")
     assert want_r[1].tolist() == [1235, 1, 0]
+    # synthetic counts at the limit: all 4096 drafts accepted past the planted
+    # mismatch, a count above K_r = 0, and a prefilling request's count ignored
+    acc = torch.tensor([k, 7, 2], dtype=torch.int32)
+    want_a = oracle.greedy_verify_ragged(xr, vocab, cu, dr, prefilling=pf, accept=acc)
+    got_a = vpa.verify_ragged(_dev(xr), vocab, w, s, _dev(cu), _dev(dr), total,
+                              prefilling=_dev(pf), accept=_dev(acc))
+    for a, b, nm in zip(got_a, want_a, ("out_tokens", "num_sampled", "num_rejected",
+                                        "target_ids")):
+        assert_same(a, b, f"ragged draft limit synthetic {nm}")
+    assert want_a[1].tolist() == [k + 1, 1, 0]
 
 
 def test_one_column_shards_and_more_shards_than_columns():
@@ -288,6 +307,16 @@ def test_ragged_verify(seed, vocab, s, n_req, kmax):
                                prefilling=_dev(pf.to(torch.uint8)))
     for g, wv in zip(got_p2[:3], want_p[:3]):
         assert_same(g, wv, "verify_ragged prefilling")
+    # synthetic accept counts, alone and together with the prefilling flags
+    acc = workloads.synthetic_counts(n_req, kmax, seed=seed + 70)
+    for flags in (None, pf):
+        want_a = oracle.greedy_verify_ragged(x_cpu, v, cu, drafts, prefilling=flags, accept=acc)
+        got_a = vpa.greedy_verify_ragged(dst, bst, cud, dd, total,
+                                         prefilling=None if flags is None else _dev(flags),
+                                         accept=_dev(acc))
+        for g, wv, nm in zip(got_a, want_a, ("out_tokens", "num_sampled", "num_rejected",
+                                             "target_ids")):
+            assert_same(g, wv, f"ragged synthetic {nm} prefilling={flags is not None}")
 
 
 def test_random_ragged_batches():
@@ -307,11 +336,13 @@ def test_random_ragged_batches():
         pf = None
         if trial % 2:
             pf = torch.tensor([rng.random() < 0.3 for _ in range(n_req)], dtype=torch.bool)
+        acc = workloads.synthetic_counts(n_req, kmax, seed=500 + trial) if trial % 3 == 1 else None
         _announce(f"random ragged {trial} V={v} S={s} R={n_req} Kmax={kmax} total={total} {dtype}"
-                  f" prefilling={None if pf is None else int(pf.sum())}")
-        want = oracle.greedy_verify_ragged(x_cpu, v, cu, drafts, prefilling=pf)
+                  f" prefilling={None if pf is None else int(pf.sum())} synthetic={acc is not None}")
+        want = oracle.greedy_verify_ragged(x_cpu, v, cu, drafts, prefilling=pf, accept=acc)
         got = vpa.verify_ragged(_dev(x_cpu), v, w, s, _dev(cu), _dev(drafts), total,
-                                prefilling=None if pf is None else _dev(pf))
+                                prefilling=None if pf is None else _dev(pf),
+                                accept=None if acc is None else _dev(acc))
         for a, b, nm in zip(got, want, ("out_tokens", "num_sampled", "num_rejected", "target_ids")):
             assert_same(a, b, f"random ragged {trial} {nm}")
 
@@ -540,6 +571,13 @@ def test_config4_full_size_4096_rows():
     got = vpa.verify_ragged(x, w.vocab, w.shard_width, w.n_shards, _dev(cu), _dev(drafts_r), total)
     for a, b, nm in zip(got, want, ("out_tokens", "num_sampled", "num_rejected", "target_ids")):
         assert_same(a, b, f"config4 ragged {nm}")
+    _announce(f"{w.name}: ragged verification, synthetic acceptance")
+    acc = workloads.synthetic_counts(w.n_req, 10, seed=4005)
+    want = oracle.greedy_verify_ragged(w.logits, w.vocab, cu, drafts_r, accept=acc)
+    got = vpa.verify_ragged(x, w.vocab, w.shard_width, w.n_shards, _dev(cu), _dev(drafts_r), total,
+                            accept=_dev(acc))
+    for a, b, nm in zip(got, want, ("out_tokens", "num_sampled", "num_rejected", "target_ids")):
+        assert_same(a, b, f"config4 ragged synthetic {nm}")
 
 
 def test_fp32_1024_rows_full_vocab():
@@ -732,8 +770,11 @@ def test_side_stream_temporaries_are_not_handed_out_early():
     with torch.cuda.stream(side):
         for _ in range(16):                      # keeps the side stream busy for about 1 ms
             busy.fill_(1)
+    # the caller's own inputs stay referenced until the side stream is done
+    cu_d, drafts_d = _dev(cu), _dev(drafts.reshape(-1))
+    torch.cuda.synchronize()
     ids, vb = vpa.top_tokens(x, v, wd, s, 8192, stream=side)
-    out = vpa.verify_ragged(x, v, wd, s, _dev(cu), _dev(drafts.reshape(-1)), r * k, stream=side)
+    out = vpa.verify_ragged(x, v, wd, s, cu_d, drafts_d, r * k, stream=side)
     # the sizes of every temporary above, allocated and filled on the default stream
     junk = [torch.empty(max(vpa.top_tokens_workspace(v, wd, s, n, 8192), 8), dtype=torch.uint8,
                         device=DEV),
@@ -748,6 +789,19 @@ def test_side_stream_temporaries_are_not_handed_out_early():
     assert torch.equal(vb.cpu().to(torch.int64) & 0xFFFFFFFF, vals)
     for a, b, nm in zip(out, want, ("out_tokens", "num_sampled", "num_rejected", "target_ids")):
         assert torch.equal(a.cpu(), b), nm
+
+
+def test_synthetic_counts_must_be_int32_per_request():
+    """accept must be a contiguous int32 device tensor with one entry per request."""
+    w = workloads.config3()
+    x = _dev(w.logits)
+    dst, bst = vpa.verify_stats(x, w.vocab, w.shard_width, w.n_shards, w.n_req, w.k)
+    drafts = torch.zeros((w.n_req, w.k), dtype=torch.int32, device=DEV)
+    for bad in (torch.zeros(w.n_req, dtype=torch.int64, device=DEV),
+                torch.zeros(w.n_req + 1, dtype=torch.int32, device=DEV),
+                torch.zeros(w.n_req, dtype=torch.int32)):
+        with pytest.raises(ValueError):
+            vpa.greedy_verify(dst, bst, drafts, accept=bad)
 
 
 def test_verify_ragged_needs_the_rows_the_requests_own():

@@ -78,7 +78,8 @@ def _bind(lib):
     lib.vpa_top_tokens.argtypes = [vp, ctypes.c_int, i64, Vocab, i64, i32, vp, sz, ep, vp, vp, vp,
                                    vp]
     lib.vpa_top_tokens.restype = st
-    lib.vpa_greedy_verify.argtypes = [vp, i32, vp, i32, i32, i64, i32, vp, vp, vp, vp, vp, vp]
+    lib.vpa_greedy_verify.argtypes = [vp, i32, vp, i32, i32, i64, i32, vp, vp, vp, vp, vp, vp,
+                                      vp]
     lib.vpa_greedy_verify.restype = st
     lib.vpa_verify_stats_rows.argtypes = [vp, ctypes.c_int, i64, Vocab, i32, i32, vp, i64, vp, i64,
                                           i64, i32, i32, vp, vp, vp]
@@ -86,7 +87,7 @@ def _bind(lib):
     lib.vpa_ragged_rows.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.vpa_ragged_rows.restype = st
     lib.vpa_greedy_verify_ragged.argtypes = [vp, i32, vp, i32, i32, i64, vp, i64, vp, vp, vp, vp,
-                                             vp, vp, vp]
+                                             vp, vp, vp, vp]
     lib.vpa_greedy_verify_ragged.restype = st
     lib.vpa_last_error.argtypes = []
     lib.vpa_last_error.restype = ctypes.c_char_p
@@ -376,10 +377,12 @@ def _verify_outputs(r, k, with_targets, dev):
 
 @_stream_arg
 def greedy_verify(draft_stats, bonus_stats, draft_ids, with_targets=True, out=None,
-                  *, stream=None):
+                  accept=None, *, stream=None):
     """Greedy verification from gathered statistics.
 
     draft_stats [S][R*K][Md][2], bonus_stats [S][R][Mb][2], draft_ids int32 [R][K].
+    accept: optional int32 device tensor [R] of synthetic accept counts (>= 0:
+    accept that many drafts whatever they are; < 0: real acceptance).
     Returns (out_tokens [R][K+1], num_sampled [R], num_rejected [R], target_ids [R][K+1] or None);
     `out` may supply those four tensors preallocated (the last may be None).
     """
@@ -392,6 +395,7 @@ def greedy_verify(draft_stats, bonus_stats, draft_ids, with_targets=True, out=No
     if bonus_stats.shape[0] != s or draft_stats.shape[1] != r * k or bonus_stats.shape[1] != r:
         raise ValueError("statistics shapes do not match draft_ids [R][K]")
     _same_device(dev, bonus_stats=bonus_stats)
+    accept = _accept_counts(accept, r, dev)
     if out is None:
         out_t, ns, nr, tg = _verify_outputs(r, k, with_targets, dev)
     else:
@@ -403,7 +407,8 @@ def greedy_verify(draft_stats, bonus_stats, draft_ids, with_targets=True, out=No
         _same_device(dev, out_tokens=out_t, num_sampled=ns, num_rejected=nr, target_ids=tg)
     _check(_on(dev, lib().vpa_greedy_verify, draft_stats.data_ptr(), draft_stats.shape[2],
                bonus_stats.data_ptr(), bonus_stats.shape[2], s, r, k, draft_ids.data_ptr(),
-               out_t.data_ptr(), ns.data_ptr(), nr.data_ptr(), _vp(tg), _stream(stream, dev)))
+               _vp(accept), out_t.data_ptr(), ns.data_ptr(), nr.data_ptr(), _vp(tg),
+               _stream(stream, dev)))
     return out_t, ns, nr, tg
 
 
@@ -467,13 +472,24 @@ def _prefilling_flags(prefilling, n_req, device):
     return prefilling
 
 
+def _accept_counts(accept, n_req, device):
+    """Optional synthetic accept counts: a contiguous int32 device tensor [R]."""
+    if accept is None:
+        return None
+    _int32_dev(accept, "accept", device)
+    if accept.numel() != n_req:
+        raise ValueError(f"accept has {accept.numel()} entries for {n_req} requests")
+    return accept
+
+
 @_stream_arg
 def greedy_verify_ragged(draft_stats, bonus_stats, cu, draft_ids, total_drafts=None,
-                         with_targets=True, prefilling=None, *, stream=None):
+                         with_targets=True, prefilling=None, accept=None, *, stream=None):
     """Ragged greedy verification from statistics.  cu int32 [R+1] cumulative
     draft counts; draft_ids int32 [total_drafts]; prefilling: optional bool or
     uint8 [R], true for a request still prefilling, which samples nothing (-1
-    in its slots, 0 sampled, 0 rejected).  Returns (out_tokens [total+R],
+    in its slots, 0 sampled, 0 rejected); accept: optional int32 [R] synthetic
+    accept counts as for greedy_verify, with K_r for K.  Returns (out_tokens [total+R],
     num_sampled [R], num_rejected [R], target_ids [total+R] or None); request
     r's K_r+1 outputs sit at offset cu[r]+r."""
     _stats_tensor(draft_stats, "draft_stats")
@@ -484,6 +500,7 @@ def greedy_verify_ragged(draft_stats, bonus_stats, cu, draft_ids, total_drafts=N
     _same_device(dev, cu=cu, draft_stats=draft_stats)
     _int32_dev(draft_ids, "draft_ids", dev)
     prefilling = _prefilling_flags(prefilling, n_req, dev)
+    accept = _accept_counts(accept, n_req, dev)
     if draft_ids.numel() != total or draft_stats.shape[1] != total or bonus_stats.shape[1] != n_req:
         raise ValueError("statistics / draft_ids do not match the offsets")
     if draft_stats.shape[0] != bonus_stats.shape[0]:
@@ -494,15 +511,15 @@ def greedy_verify_ragged(draft_stats, bonus_stats, cu, draft_ids, total_drafts=N
     tg = buf[per + 2 * n_req:] if with_targets else None
     _check(_on(dev, lib().vpa_greedy_verify_ragged, draft_stats.data_ptr(), draft_stats.shape[2],
                bonus_stats.data_ptr(), bonus_stats.shape[2], bonus_stats.shape[0], n_req,
-               cu.data_ptr(), total, draft_ids.data_ptr(), _vp(prefilling), out.data_ptr(),
-               ns.data_ptr(), nr.data_ptr(), _vp(tg), _stream(stream, dev)))
+               cu.data_ptr(), total, draft_ids.data_ptr(), _vp(prefilling), _vp(accept),
+               out.data_ptr(), ns.data_ptr(), nr.data_ptr(), _vp(tg), _stream(stream, dev)))
     return out, ns, nr, tg
 
 
 @_stream_arg
 def verify_ragged(logits, vocab, shard_width, n_shards, cu, draft_ids, total_drafts=None,
                   block_draft=DRAFT_BLOCK, block_bonus=BONUS_BLOCK, with_targets=True,
-                  prefilling=None, *, stream=None):
+                  prefilling=None, accept=None, *, stream=None):
     """The whole ragged verification on one GPU: row lists, statistics, finish.
     logits must hold the total_drafts + R rows the requests own."""
     total = _total_drafts(cu, total_drafts)
@@ -512,5 +529,5 @@ def verify_ragged(logits, vocab, shard_width, n_shards, cu, draft_ids, total_dra
     draft_rows, bonus_rows = ragged_rows(cu, total, stream=stream)
     dst, bst = verify_stats_rows(logits, vocab, shard_width, n_shards, draft_rows, bonus_rows,
                                  block_draft, block_bonus, stream=stream)
-    return greedy_verify_ragged(dst, bst, cu, draft_ids, total, with_targets, prefilling,
+    return greedy_verify_ragged(dst, bst, cu, draft_ids, total, with_targets, prefilling, accept,
                                 stream=stream)

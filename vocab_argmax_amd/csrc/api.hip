@@ -170,6 +170,63 @@ vpa_status set_items(vpa::SegTask& t, int64_t n_rows, const char* what) {
     return ok();
 }
 
+// A validated vpa_top_tokens call: the statistics task over all S shards of
+// every row ([S][n_rows][M], as vpa_block_stats cuts them), the workspace
+// bytes it needs, and the resolved epilogue.  (Cutting each row at global
+// block edges only, ignoring shard edges, and cutting the launch's last rows
+// into smaller blocks were both measured; neither was faster.)
+struct TopCall {
+    vpa::SegTask task;
+    size_t ws_bytes;
+    Epi epi;
+    int esize;
+};
+
+vpa_status check_top_tokens(const void* logits, vpa_dtype dtype, int64_t ld, const vpa_vocab& v,
+                            int64_t n_rows, int32_t block, const vpa_epilogue* epi,
+                            const int32_t* ids, const uint32_t* val_bits, int64_t* mapped,
+                            TopCall& c) {
+    vpa_status st = check_logits_task(dtype, ld, v, 0, v.n_shards, block, c.task);
+    if (st != VPA_OK)
+        return st;
+    if ((st = check_epilogue(epi, v.vocab, mapped, c.epi)) != VPA_OK)
+        return st;
+    if (n_rows < 0)
+        return fail(VPA_ERR_INVALID, "n_rows %lld < 0", (long long)n_rows);
+    if ((st = set_items(c.task, n_rows, "vpa_top_tokens")) != VPA_OK)
+        return st;
+    c.ws_bytes = (size_t)c.task.n_items * sizeof(vpa_stat);
+    if (n_rows == 0)
+        return ok();
+    if ((st = check_logits_ptr(logits, dtype)) != VPA_OK)
+        return st;
+    if (!ids || !aligned(ids, 4) || (val_bits && !aligned(val_bits, 4)))
+        return fail(VPA_ERR_INVALID, "ids is NULL, or ids/val_bits not 4-byte aligned");
+    c.esize = esize_of(dtype);
+    c.task.base = (const unsigned char*)logits;
+    c.task.logits_rows = n_rows;
+    vpa::SegTask none{};
+    if ((st = check_dispatch(vpa::block_stats_threads(c.esize, c.task, none),
+                             "vpa_top_tokens (statistics)")) != VPA_OK ||
+        (st = check_dispatch(vpa::combine_threads((int32_t)n_rows), "vpa_top_tokens (combine)")) !=
+            VPA_OK)
+        return st;
+    return ok();
+}
+
+// The two launches of a checked call, with its statistics in `ws`.
+vpa_status launch_top_tokens(TopCall& c, vpa_stat* ws, int32_t* ids, uint32_t* val_bits,
+                             int64_t* mapped, hipStream_t stream) {
+    c.task.stats = ws;
+    vpa::SegTask none{};
+    hipError_t e = vpa::launch_block_stats(c.esize, c.task, none, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "vpa_top_tokens statistics launch");
+    e = vpa::launch_combine(ws, c.task.n_local, c.task.n_rows, c.task.m, c.epi.d2t, c.epi.d2t_len,
+                            c.epi.scale, ids, val_bits, mapped, stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "vpa_top_tokens combine launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -358,48 +415,22 @@ vpa_status vpa_top_tokens(const void* logits, vpa_dtype dtype, int64_t ld, vpa_v
                           int64_t n_rows, int32_t block, void* workspace, size_t workspace_bytes,
                           const vpa_epilogue* epi, int32_t* ids, uint32_t* val_bits,
                           int64_t* mapped, void* stream) {
-    vpa::SegTask t;
-    vpa_status st = check_logits_task(dtype, ld, v, 0, v.n_shards, block, t);
-    if (st != VPA_OK)
+    TopCall c;
+    vpa_status st = check_top_tokens(logits, dtype, ld, v, n_rows, block, epi, ids, val_bits,
+                                     mapped, c);
+    if (st != VPA_OK || n_rows == 0)
         return st;
-    Epi ep;
-    if ((st = check_epilogue(epi, v.vocab, mapped, ep)) != VPA_OK)
-        return st;
-    if (n_rows < 0)
-        return fail(VPA_ERR_INVALID, "n_rows %lld < 0", (long long)n_rows);
-    if ((st = set_items(t, n_rows, "vpa_top_tokens")) != VPA_OK)
-        return st;
-    if (n_rows == 0)
-        return ok();
-    if ((st = check_logits_ptr(logits, dtype)) != VPA_OK)
-        return st;
-    const size_t need = vpa_top_tokens_workspace(v, n_rows, block);
-    if (!workspace || !aligned(workspace, 8) || workspace_bytes < need)
-        return fail(VPA_ERR_INVALID, "workspace NULL, unaligned or smaller than %zu bytes", need);
-    if (!ids || !aligned(ids, 4) || (val_bits && !aligned(val_bits, 4)))
-        return fail(VPA_ERR_INVALID, "ids is NULL, or ids/val_bits not 4-byte aligned");
-    t.base = (const unsigned char*)logits;
-    t.logits_rows = n_rows;
-    t.stats = (vpa_stat*)workspace;
-    vpa::SegTask none{};
-    if ((st = check_dispatch(vpa::block_stats_threads(esize_of(dtype), t, none),
-                             "vpa_top_tokens (statistics)")) != VPA_OK ||
-        (st = check_dispatch(vpa::combine_threads((int32_t)n_rows), "vpa_top_tokens (combine)")) !=
-            VPA_OK)
-        return st;
-    hipError_t e = vpa::launch_block_stats(esize_of(dtype), t, none, (hipStream_t)stream);
-    if (e != hipSuccess)
-        return hip_fail(e, "vpa_top_tokens statistics launch");
-    e = vpa::launch_combine(t.stats, v.n_shards, (int32_t)n_rows, t.m, ep.d2t, ep.d2t_len,
-                            ep.scale, ids, val_bits, mapped, (hipStream_t)stream);
-    return e == hipSuccess ? ok() : hip_fail(e, "vpa_top_tokens combine launch");
+    if (!workspace || !aligned(workspace, 8) || workspace_bytes < c.ws_bytes)
+        return fail(VPA_ERR_INVALID, "workspace NULL, unaligned or smaller than %zu bytes",
+                    c.ws_bytes);
+    return launch_top_tokens(c, (vpa_stat*)workspace, ids, val_bits, mapped, (hipStream_t)stream);
 }
 
 vpa_status vpa_greedy_verify(const vpa_stat* draft_stats, int32_t m_draft,
                              const vpa_stat* bonus_stats, int32_t m_bonus, int32_t n_shards,
                              int64_t n_req, int32_t k, const int32_t* draft_ids,
-                             int32_t* out_tokens, int32_t* num_sampled, int32_t* num_rejected,
-                             int32_t* target_ids, void* stream) {
+                             const int32_t* accept, int32_t* out_tokens, int32_t* num_sampled,
+                             int32_t* num_rejected, int32_t* target_ids, void* stream) {
     if (n_shards < 1 || m_draft < 1 || m_bonus < 1 || (int64_t)n_shards * m_draft > INT32_MAX ||
         (int64_t)n_shards * m_bonus > INT32_MAX)
         return fail(VPA_ERR_INVALID, "n_shards %d / m_draft %d / m_bonus %d invalid",
@@ -415,14 +446,16 @@ vpa_status vpa_greedy_verify(const vpa_stat* draft_stats, int32_t m_draft,
     if (!draft_ids || !out_tokens || !num_sampled || !num_rejected)
         return fail(VPA_ERR_INVALID, "draft_ids/out_tokens/num_sampled/num_rejected is NULL");
     if (!aligned(draft_ids, 4) || !aligned(out_tokens, 4) || !aligned(num_sampled, 4) ||
-        !aligned(num_rejected, 4) || (target_ids && !aligned(target_ids, 4)))
+        !aligned(num_rejected, 4) || (target_ids && !aligned(target_ids, 4)) ||
+        (accept && !aligned(accept, 4)))
         return fail(VPA_ERR_INVALID, "an int32 array is not 4-byte aligned");
     vpa_status st = check_dispatch(vpa::greedy_verify_threads((int32_t)n_req, k), "vpa_greedy_verify");
     if (st != VPA_OK)
         return st;
     hipError_t e = vpa::launch_greedy_verify(draft_stats, m_draft, bonus_stats, m_bonus, n_shards,
-                                             (int32_t)n_req, k, draft_ids, out_tokens, num_sampled,
-                                             num_rejected, target_ids, (hipStream_t)stream);
+                                             (int32_t)n_req, k, draft_ids, accept, out_tokens,
+                                             num_sampled, num_rejected, target_ids,
+                                             (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "vpa_greedy_verify launch");
 }
 
@@ -430,9 +463,9 @@ vpa_status vpa_greedy_verify_ragged(const vpa_stat* draft_stats, int32_t m_draft
                                     const vpa_stat* bonus_stats, int32_t m_bonus,
                                     int32_t n_shards, int64_t n_req, const int32_t* cu,
                                     int64_t total_drafts, const int32_t* draft_ids,
-                                    const uint8_t* prefilling, int32_t* out_tokens,
-                                    int32_t* num_sampled, int32_t* num_rejected,
-                                    int32_t* target_ids, void* stream) {
+                                    const uint8_t* prefilling, const int32_t* accept,
+                                    int32_t* out_tokens, int32_t* num_sampled,
+                                    int32_t* num_rejected, int32_t* target_ids, void* stream) {
     if (n_shards < 1 || m_draft < 1 || m_bonus < 1 || (int64_t)n_shards * m_draft > INT32_MAX ||
         (int64_t)n_shards * m_bonus > INT32_MAX)
         return fail(VPA_ERR_INVALID, "n_shards %d / m_draft %d / m_bonus %d invalid",
@@ -448,7 +481,7 @@ vpa_status vpa_greedy_verify_ragged(const vpa_stat* draft_stats, int32_t m_draft
     if (!aligned(cu, 4) || !aligned(bonus_stats, 8) || (draft_stats && !aligned(draft_stats, 8)) ||
         (draft_ids && !aligned(draft_ids, 4)) || !aligned(out_tokens, 4) ||
         !aligned(num_sampled, 4) || !aligned(num_rejected, 4) ||
-        (target_ids && !aligned(target_ids, 4)))
+        (target_ids && !aligned(target_ids, 4)) || (accept && !aligned(accept, 4)))
         return fail(VPA_ERR_INVALID, "a pointer is misaligned");
     vpa_status st =
         check_dispatch(vpa::greedy_verify_ragged_threads((int32_t)n_req), "vpa_greedy_verify_ragged");
@@ -456,8 +489,8 @@ vpa_status vpa_greedy_verify_ragged(const vpa_stat* draft_stats, int32_t m_draft
         return st;
     hipError_t e = vpa::launch_greedy_verify_ragged(
         draft_stats, m_draft, bonus_stats, m_bonus, n_shards, (int32_t)n_req, cu,
-        (int32_t)total_drafts, draft_ids, prefilling, out_tokens, num_sampled, num_rejected,
-        target_ids, (hipStream_t)stream);
+        (int32_t)total_drafts, draft_ids, prefilling, accept, out_tokens, num_sampled,
+        num_rejected, target_ids, (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "vpa_greedy_verify_ragged launch");
 }
 

@@ -76,8 +76,8 @@ hipError_t launch_combine(const vpa_stat* stats, int32_t n_shards, int32_t n_row
 hipError_t launch_greedy_verify(const vpa_stat* draft_stats, int32_t m_draft,
                                 const vpa_stat* bonus_stats, int32_t m_bonus, int32_t n_shards,
                                 int32_t n_req, int32_t k, const int32_t* draft_ids,
-                                int32_t* out_tokens, int32_t* num_sampled, int32_t* num_rejected,
-                                int32_t* target_ids, hipStream_t stream);
+                                const int32_t* accept, int32_t* out_tokens, int32_t* num_sampled,
+                                int32_t* num_rejected, int32_t* target_ids, hipStream_t stream);
 
 hipError_t launch_ragged_rows(const int32_t* cu, int32_t n_req, int32_t total_drafts,
                               int32_t* draft_rows, int32_t* bonus_rows, hipStream_t stream);
@@ -86,8 +86,9 @@ hipError_t launch_greedy_verify_ragged(const vpa_stat* draft_stats, int32_t m_dr
                                        const vpa_stat* bonus_stats, int32_t m_bonus,
                                        int32_t n_shards, int32_t n_req, const int32_t* cu,
                                        int32_t total_drafts, const int32_t* draft_ids,
-                                       const uint8_t* prefilling, int32_t* out_tokens,
-                                       int32_t* num_sampled, int32_t* num_rejected,
-                                       int32_t* target_ids, hipStream_t stream);
+                                       const uint8_t* prefilling, const int32_t* accept,
+                                       int32_t* out_tokens, int32_t* num_sampled,
+                                       int32_t* num_rejected, int32_t* target_ids,
+                                       hipStream_t stream);
 
 }  // namespace vpa

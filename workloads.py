@@ -85,6 +85,16 @@ def compose_drafts(target_ids: torch.Tensor, plan: torch.Tensor, uniform: torch.
     return torch.where(plan == -1, torch.full_like(out, -1), out)
 
 
+def synthetic_counts(n_req: int, k_max: int, seed: int, p_real: float = 0.25) -> torch.Tensor:
+    """Synthetic accept counts int32 [R]: -1 (real acceptance) with probability
+    p_real, otherwise a uniform draw from [0, k_max + 2] (so that counts past
+    the draft count occur too).  The acceptance itself is not computed here."""
+    g = _gen(seed, "cpu")
+    counts = torch.randint(0, k_max + 3, (n_req,), generator=g, dtype=torch.int64)
+    real = torch.rand(n_req, generator=g) < p_real
+    return torch.where(real, torch.full_like(counts, -1), counts).to(torch.int32)
+
+
 def config1() -> Workload:
     """4 rows x vocab 1000 fp32 ~N(0,1), one shard, block 256; rows 1 and 3 carry a
     planted exact tie of the row maximum at ids 17 and 903."""
