@@ -214,6 +214,27 @@ vpa_status vpa_top_tokens(const void* logits, vpa_dtype dtype, int64_t ld, vpa_v
                           const vpa_epilogue* epi, int32_t* ids, uint32_t* val_bits,
                           int64_t* mapped, void* stream);
 
+/* vpa_top_tokens for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments and results as vpa_top_tokens without the workspace: the
+ * statistics go to a device array the library holds, one copy of
+ * VPA_NOALLOC_WORKSPACE_BYTES per GPU it runs on, kept until the process
+ * ends.  The call makes no allocation and no memset; the first call on a
+ * device looks the array's address up once (hipGetSymbolAddress).
+ *  - A call needing more statistics bytes than VPA_NOALLOC_WORKSPACE_BYTES
+ *    (vpa_top_tokens_workspace) returns VPA_ERR_INVALID and enqueues
+ *    nothing; at 8192-column blocks that allows 16384 rows of a
+ *    200064-entry vocabulary over 8 shards.
+ *  - Every call on one GPU shares that GPU's array, and the array keeps the
+ *    last call's contents (nothing in it needs to start at zero): calls that
+ *    overlap on one GPU (on different streams) race on it and must be
+ *    serialised by the caller. */
+#define VPA_NOALLOC_WORKSPACE_BYTES ((size_t)4 << 20)
+vpa_status vpa_top_tokens_noalloc(const void* logits, vpa_dtype dtype, int64_t ld, vpa_vocab v,
+                                  int64_t n_rows, int32_t block, const vpa_epilogue* epi,
+                                  int32_t* ids, uint32_t* val_bits, int64_t* mapped,
+                                  void* stream);
+
 /* Greedy verification from gathered statistics (PR #62604, "Purpose" item 1
  * and "Test Plan"): the target token of each position is the combined
  * argmax of its row; drafts are accepted while they equal their target;

@@ -300,3 +300,23 @@ def test_sizes_past_the_limits_are_rejected_without_overflow(lib):
                               None, FAKE, None, None, None) == vpa.VPA_ERR_INVALID
     assert lib.vpa_verify_stats(FAKE, vpa.VPA_BF16, 1000, V(1000, 125, 8), 0, 8, huge, 3, 8192,
                                 1024, FAKE, FAKE, None) == vpa.VPA_ERR_INVALID
+
+
+def test_noalloc_top_tokens_rejects_beyond_its_array(lib):
+    """vpa_top_tokens_noalloc validates like vpa_top_tokens and refuses, before
+    any HIP call, a call whose statistics exceed VPA_NOALLOC_WORKSPACE_BYTES."""
+    voc = V(200064, 25008, 8)                    # 32 statistics (256 bytes) per row
+    limit = vpa.NOALLOC_WORKSPACE_BYTES
+    assert lib.vpa_top_tokens_workspace(voc, 16384, 8192) == limit
+    call = lambda n, **kw: lib.vpa_top_tokens_noalloc(
+        kw.get("logits", FAKE), vpa.VPA_BF16, kw.get("ld", 200064), voc, n, kw.get("block", 8192),
+        None, kw.get("ids", FAKE), None, None, None)
+    assert call(16385) == vpa.VPA_ERR_INVALID
+    assert "VPA_NOALLOC_WORKSPACE_BYTES" in vpa.last_error()
+    assert call(0) == vpa.VPA_OK                 # empty batch: nothing to do
+    assert call(4, ids=None) == vpa.VPA_ERR_INVALID
+    assert call(4, logits=FAKE_ODD) == vpa.VPA_ERR_INVALID
+    assert call(4, ld=200063) == vpa.VPA_ERR_INVALID
+    assert call(4, block=0) == vpa.VPA_ERR_INVALID
+    assert lib.vpa_top_tokens_noalloc(FAKE, vpa.VPA_BF16, 200064, voc, 4, 8192,
+                                      EPI(scale=-1.0), FAKE, None, None, None) == vpa.VPA_ERR_INVALID

@@ -37,7 +37,9 @@ BONUS_BLOCK = 1024   # global block size for the bonus position
 # Every symbol include/vpa.h declares.
 SYMBOLS = ("vpa_stats_slots", "vpa_block_stats", "vpa_verify_stats", "vpa_verify_stats_rows",
            "vpa_ragged_rows", "vpa_combine_stats", "vpa_top_tokens_workspace", "vpa_top_tokens",
-           "vpa_greedy_verify", "vpa_greedy_verify_ragged", "vpa_last_error")
+           "vpa_top_tokens_noalloc", "vpa_greedy_verify", "vpa_greedy_verify_ragged",
+           "vpa_last_error")
+NOALLOC_WORKSPACE_BYTES = 4 << 20   # VPA_NOALLOC_WORKSPACE_BYTES
 
 
 class VpaError(RuntimeError):
@@ -78,6 +80,9 @@ def _bind(lib):
     lib.vpa_top_tokens.argtypes = [vp, ctypes.c_int, i64, Vocab, i64, i32, vp, sz, ep, vp, vp, vp,
                                    vp]
     lib.vpa_top_tokens.restype = st
+    lib.vpa_top_tokens_noalloc.argtypes = [vp, ctypes.c_int, i64, Vocab, i64, i32, ep, vp, vp, vp,
+                                           vp]
+    lib.vpa_top_tokens_noalloc.restype = st
     lib.vpa_greedy_verify.argtypes = [vp, i32, vp, i32, i32, i64, i32, vp, vp, vp, vp, vp, vp,
                                       vp]
     lib.vpa_greedy_verify.restype = st
@@ -359,6 +364,37 @@ def top_tokens(logits, vocab, shard_width, n_shards, block=DRAFT_BLOCK, workspac
     _check(_on(dev, lib().vpa_top_tokens, logits.data_ptr(), _dtype_code(logits), ld, voc, n,
                block, workspace.data_ptr(), workspace.numel() * workspace.element_size(), epi,
                ids.data_ptr(), val_bits.data_ptr(), _vp(mapped if d2t is not None else None),
+               _stream(stream, dev)))
+    return (ids, val_bits) if d2t is None else (ids, val_bits, mapped)
+
+
+@_stream_arg
+def top_tokens_noalloc(logits, vocab, shard_width, n_shards, block=DRAFT_BLOCK, ids=None,
+                       val_bits=None, d2t=None, scale=1.0, mapped=None, *, stream=None):
+    """top_tokens with the statistics in the library's own device array
+    (vpa_top_tokens_noalloc): the C call allocates nothing, so it can run
+    under graph capture or where allocation is forbidden; pass ids,
+    val_bits (and mapped) to keep this function from allocating them.  The
+    statistics must fit NOALLOC_WORKSPACE_BYTES; calls that overlap on one
+    GPU share that array and must not run concurrently."""
+    ld = _logits_ld(logits)
+    n = logits.shape[0]
+    dev = logits.device
+    if ids is None and val_bits is None:
+        buf = torch.empty((2, n), dtype=torch.int32, device=dev)
+        ids, val_bits = buf[0], buf[1]
+    else:
+        ids = (torch.empty(n, dtype=torch.int32, device=dev) if ids is None
+               else _out_tensor(ids, "ids", torch.int32, n, dev))
+        val_bits = (torch.empty(n, dtype=torch.int32, device=dev) if val_bits is None
+                    else _out_tensor(val_bits, "val_bits", torch.int32, n, dev))
+    if d2t is not None:
+        mapped = (torch.empty(n, dtype=torch.int64, device=dev) if mapped is None
+                  else _out_tensor(mapped, "mapped", torch.int64, n, dev))
+    epi, _keep = _epilogue(d2t, scale, dev)
+    _check(_on(dev, lib().vpa_top_tokens_noalloc, logits.data_ptr(), _dtype_code(logits), ld,
+               _vocab(vocab, shard_width, n_shards), n, block, epi, ids.data_ptr(),
+               val_bits.data_ptr(), _vp(mapped if d2t is not None else None),
                _stream(stream, dev)))
     return (ids, val_bits) if d2t is None else (ids, val_bits, mapped)
 

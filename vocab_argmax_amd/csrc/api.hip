@@ -5,9 +5,19 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+#include <mutex>
 #include <string>
 
 #include "vpa_internal.h"
+
+// The statistics of vpa_top_tokens_noalloc: a file-scope device array.
+// Every GPU the library runs on holds its own copy until the process ends.
+// Host code never passes the array's name to a kernel (on the host it is a
+// stand-in, not a device address): it passes the address
+// hipGetSymbolAddress returns for the current device, kept per device
+// (scratch_of_current_device below).
+static __device__ __align__(256) vpa_stat scratch[VPA_NOALLOC_WORKSPACE_BYTES / sizeof(vpa_stat)];
 
 namespace {
 
@@ -227,6 +237,36 @@ vpa_status launch_top_tokens(TopCall& c, vpa_stat* ws, int32_t* ids, uint32_t* v
     return e == hipSuccess ? ok() : hip_fail(e, "vpa_top_tokens combine launch");
 }
 
+constexpr int kMaxDevices = 64;
+std::atomic<vpa_stat*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch`, looked up once per device.
+vpa_status scratch_of_current_device(vpa_stat** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "vpa_top_tokens_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(VPA_ERR_UNSUPPORTED, "vpa_top_tokens_noalloc: device %d beyond the %d supported",
+                    dev, kMaxDevices);
+    vpa_stat* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            void* addr = nullptr;
+            e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess)
+                return hip_fail(e, "vpa_top_tokens_noalloc: hipGetSymbolAddress(scratch)");
+            p = (vpa_stat*)addr;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -424,6 +464,26 @@ vpa_status vpa_top_tokens(const void* logits, vpa_dtype dtype, int64_t ld, vpa_v
         return fail(VPA_ERR_INVALID, "workspace NULL, unaligned or smaller than %zu bytes",
                     c.ws_bytes);
     return launch_top_tokens(c, (vpa_stat*)workspace, ids, val_bits, mapped, (hipStream_t)stream);
+}
+
+vpa_status vpa_top_tokens_noalloc(const void* logits, vpa_dtype dtype, int64_t ld, vpa_vocab v,
+                                  int64_t n_rows, int32_t block, const vpa_epilogue* epi,
+                                  int32_t* ids, uint32_t* val_bits, int64_t* mapped,
+                                  void* stream) {
+    TopCall c;
+    vpa_status st = check_top_tokens(logits, dtype, ld, v, n_rows, block, epi, ids, val_bits,
+                                     mapped, c);
+    if (st != VPA_OK || n_rows == 0)
+        return st;
+    if (c.ws_bytes > (size_t)VPA_NOALLOC_WORKSPACE_BYTES)
+        return fail(VPA_ERR_INVALID,
+                    "vpa_top_tokens_noalloc: %lld rows need %zu bytes of statistics, more than the "
+                    "%zu the library holds (VPA_NOALLOC_WORKSPACE_BYTES); use vpa_top_tokens",
+                    (long long)n_rows, c.ws_bytes, (size_t)VPA_NOALLOC_WORKSPACE_BYTES);
+    vpa_stat* ws = nullptr;
+    if ((st = scratch_of_current_device(&ws)) != VPA_OK)
+        return st;
+    return launch_top_tokens(c, ws, ids, val_bits, mapped, (hipStream_t)stream);
 }
 
 vpa_status vpa_greedy_verify(const vpa_stat* draft_stats, int32_t m_draft,
