@@ -24,12 +24,16 @@ of vpa_verify_stats, whose average duration HIP events on the launch stream
 measure over back-to-back launches right after the timed steps (median of 5
 windows), against MI355X's 8 TB/s HBM peak; top_tokens_rows_sweep = the fused
 argmax alone at 1024, 2048 and 4096 bf16 rows and 1024 fp32 rows, alternating
-two input buffers; small_configs_us = the 32-row argmax and the 24 x 4-row
-verification from Python and replayed from HIP graphs; read_ceiling = a plain
-persistent read of the same two 1.64 GB buffers (libvpa_probe.so), the
-practical HBM read rate of this GPU, beside which the roofline's achieved
+two input buffers; target_check = the 1024-, 2048- and 4096-row argmax against
+the 80 % bandwidth target; per_config = configurations 1-3 (4-row fp32
+argmax, 32-row argmax, 24 x 4-row verification) from Python and replayed from
+HIP graphs, with algorithmic bytes; read_ceiling = a plain persistent read of
+the same two 1.64 GB buffers and of their first 1024 rows (libvpa_probe.so),
+the practical HBM read rate of this GPU, beside which the roofline's achieved
 rate is set; cpu_baseline = the CPU oracle timed on this host on the same
-step.
+step, and on configurations 1-3 (median of 5) with parity against the GPU.
+Every per-call measurement is preceded by 20 ms of the same call, so that no
+window starts inside a clock transient.
 """
 import argparse
 import hashlib
@@ -63,8 +67,67 @@ def algorithmic_bytes():
     m_tt, m_d, m_b = slots(W, S, B_DRAFT), slots(W, S, B_DRAFT), slots(W, S, B_BONUS)
     top_tokens = N_ROWS * (V * e + S * m_tt * 8 * 2 + 8)          # logits + stats w/r + id/value
     verify_stats = R * K * (V * e + S * m_d * 8) + R * (V * e + S * m_b * 8)
-    greedy = R * (K * S * m_d * 8 + S * m_b * 8 + 4 * K + 4 * (K + 1) * 2 + 8)
+    greedy = R * (K * S * m_d * 8 + S * m_b * 8 + 4 * K + 4 * (K + 1) + 8)
     return {"top_tokens": top_tokens, "verify_stats": verify_stats, "greedy_verify": greedy}
+
+
+def top_tokens_bytes(n_rows, vocab, esize, n_shards, m):
+    """Algorithmic bytes of one top_tokens call: valid logits, statistics
+    written and read back, id and value per row."""
+    return n_rows * (vocab * esize + n_shards * m * 8 * 2 + 8)
+
+
+def verify_bytes(n_req, k, vocab, esize, n_shards, m_draft, m_bonus):
+    """Algorithmic bytes of verify_stats + greedy_verify (no target ids)."""
+    stats = (n_req * k * (vocab * esize + n_shards * m_draft * 8)
+             + n_req * (vocab * esize + n_shards * m_bonus * 8))
+    finish = n_req * (k * n_shards * m_draft * 8 + n_shards * m_bonus * 8 + 4 * k
+                      + 4 * (k + 1) + 8)
+    return stats + finish
+
+
+def oracle_per_config(works, gpu_calls, cfg_bytes, dev):
+    """The CPU oracle on configurations 1-3: median of 5 timed runs on one
+    pinned core, and whether the GPU calls' outputs equal the oracle's."""
+    import oracle
+    import torch
+    import workloads
+    w1, w2, w3 = works
+    out = {}
+
+    def timed5(fn):
+        ts = []
+        for _ in range(5):
+            t0 = time.perf_counter()
+            res = fn()
+            ts.append(time.perf_counter() - t0)
+        return sorted(ts)[2], res
+
+    for name, w in (("config1", w1), ("config2", w2)):
+        t, (ids, vals) = timed5(lambda: oracle.argmax(w.logits, w.vocab))
+        g_ids, g_vals = gpu_calls[name]()
+        parity = (torch.equal(g_ids.cpu(), ids)
+                  and torch.equal(g_vals.cpu().to(torch.int64) & 0xFFFFFFFF, vals))
+        out[name] = {"oracle_us_median5": t * 1e6, "rows_per_s": w.logits.shape[0] / t,
+                     "gbps": cfg_bytes[name] / t / 1e9, "parity_with_gpu": bool(parity)}
+    draft_rows, bonus_rows = oracle.verify_rows(w3.n_req, w3.k)
+    tgt, _ = oracle.argmax(w3.logits, w3.vocab)
+    drafts = workloads.compose_drafts(tgt.reshape(w3.n_req, w3.k + 1), w3.draft_plan,
+                                      w3.draft_uniform)
+
+    def verify():
+        dst = oracle.block_stats(w3.logits, w3.vocab, w3.shard_width, w3.n_shards, 8192,
+                                 rows=draft_rows)
+        bst = oracle.block_stats(w3.logits, w3.vocab, w3.shard_width, w3.n_shards, 1024,
+                                 rows=bonus_rows)
+        return oracle.greedy_verify(dst, bst, drafts)
+    t, want = timed5(verify)
+    got = gpu_calls["config3"](drafts.to(dev))
+    parity = all(torch.equal(a.cpu(), b) for a, b in zip(got[:3], want[:3]))
+    out["config3"] = {"oracle_us_median5": t * 1e6, "rows_per_s": w3.n_req * (w3.k + 1) / t,
+                      "gbps": cfg_bytes["config3"] / t / 1e9, "parity_with_gpu": bool(parity)}
+    out["cores"] = 1
+    return out
 
 
 def kernel_source_hash():
@@ -246,6 +309,15 @@ def main():
     def per_call(fn, n=n_k):
         return sorted(timed(fn, n)[1] / n for _ in range(REPEATS))[REPEATS // 2]
 
+    def settle(fn, seconds=0.02):
+        """Run fn back to back for 20 ms before a measurement window, so that
+        the window does not start inside a clock transient after host-side
+        work (allocations, graph capture) left the GPU idle."""
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            fn()
+        torch.cuda.synchronize()
+
     tt_s = per_call(top)
     vs_s = per_call(vstats)
     gv_s = per_call(finish)
@@ -266,6 +338,7 @@ def main():
         def call():
             vpa.top_tokens(views[flip[0]], V, W, S, B_DRAFT, workspace=wsn, ids=idn, val_bits=vln)
             flip[0] ^= 1
+        settle(call)
         t = per_call(call, 2 * n_k)
         alg_b = n_rows * (V * esize + S * m * 8 * 2 + 8)
         return {"us": t * 1e6, "rows_per_s": n_rows / t, "gbps": alg_b / t / 1e9,
@@ -280,7 +353,7 @@ def main():
     # the practical read ceiling: a read-only persistent kernel over the same
     # two buffers, alternating, timed like the calls above (reported as null,
     # with a warning, if the probe library was not built)
-    from vocab_argmax_amd import read_probe
+    import hbm_probe as read_probe
     read_ceiling = None
     try:
         n_wg = read_probe.default_workgroups(dev)
@@ -295,8 +368,19 @@ def main():
         def probe_call():
             probe_bytes[0] = read_probe.read(probe_bufs[probe_flip[0]], sink, n_wg)
             probe_flip[0] ^= 1
+        settle(probe_call)
         probe_s = per_call(probe_call, 2 * n_k)
         probe_gbps = probe_bytes[0] / probe_s / 1e9
+        # the same read over the first 1024 rows of each buffer (410 MB): the
+        # attainable rate at the size of the 1024-row argmax
+        probe_small = (xd[:1024], xt[:1024])
+        small_bytes = [0]
+
+        def probe_small_call():
+            small_bytes[0] = read_probe.read(probe_small[probe_flip[0]], sink, n_wg)
+            probe_flip[0] ^= 1
+        settle(probe_small_call)
+        probe_small_s = per_call(probe_small_call, 2 * n_k)
         read_ceiling = {
             "probe": (f"read-only persistent grid ({n_wg} workgroups of 256 threads, "
                       f"{read_probe.WORKGROUPS_PER_CU} per CU), 16-byte non-temporal loads in "
@@ -305,6 +389,9 @@ def main():
             "avg_launch_us": probe_s * 1e6,
             "gbps": probe_gbps,
             "frac_of_peak": probe_gbps / PEAK_HBM_GBPS,
+            "rows_1024": {"bytes_per_launch": small_bytes[0], "avg_launch_us": probe_small_s * 1e6,
+                          "gbps": small_bytes[0] / probe_small_s / 1e9,
+                          "frac_of_peak": small_bytes[0] / probe_small_s / 1e9 / PEAK_HBM_GBPS},
         }
 
     ms_step = max(wall, gpu) * 1e3 / args.steps
@@ -355,56 +442,87 @@ def main():
             "algorithmic_bytes_per_launch": alg["verify_stats"],
             "avg_launch_us": vs_s * 1e6,
         },
+        "target_check": {
+            "target": ("fused argmax (vpa_top_tokens, statistics and combine launches) over "
+                       f"{V}-entry bf16 rows at >= 1024 rows: >= 80 % of {PEAK_HBM_GBPS:.0f} GB/s"),
+            "rows": {n: {"hbm_frac": sweep[f"bf16_n{n}"]["hbm_frac"],
+                         "met": sweep[f"bf16_n{n}"]["hbm_frac"] >= 0.80}
+                     for n in (1024, 2048, N_ROWS)},
+        },
         "read_ceiling": read_ceiling,
         "cpu_baseline": None,
     }
-    # the small configurations of the pages' workloads (latency-bound; reported only)
-    small = {}
-    w2 = workloads.config2(device=dev)
-    x2 = w2.logits
-    small["top_tokens_32x151936_s2"] = per_call(
-        lambda: vpa.top_tokens(x2, w2.vocab, w2.shard_width, w2.n_shards, 8192)) * 1e6
-    w3 = workloads.config3(device=dev)
-    x3 = w3.logits
+    # configurations 1-3 of the pages' workloads: eager calls from Python and
+    # the same calls replayed from a HIP graph of 20 back-to-back copies (the
+    # GPU time a decode loop would see); latency-bound, reported only
+    w1, w2, w3 = workloads.config1(), workloads.config2(), workloads.config3()
+    x1, x2, x3 = w1.logits.to(dev), w2.logits.to(dev), w3.logits.to(dev)
     d3 = torch.zeros((w3.n_req, w3.k), dtype=torch.int32, device=dev)
-
-    def verify3():
-        st = vpa.verify_stats(x3, w3.vocab, w3.shard_width, w3.n_shards, w3.n_req, w3.k)
-        vpa.greedy_verify(st[0], st[1], d3, with_targets=False)
-    small["verify_24x4_rows_200064_s4"] = per_call(verify3) * 1e6
-    # the same two calls captured once in a HIP graph and replayed: GPU time
-    # without the Python launch cost (a decode loop would replay like this)
+    ws1 = torch.empty(vpa.top_tokens_workspace(w1.vocab, w1.shard_width, w1.n_shards, 4, 256),
+                      dtype=torch.uint8, device=dev)
     ws2 = torch.empty(vpa.top_tokens_workspace(w2.vocab, w2.shard_width, w2.n_shards, 32),
                       dtype=torch.uint8, device=dev)
+
+    def top1():
+        return vpa.top_tokens(x1, w1.vocab, w1.shard_width, w1.n_shards, 256, workspace=ws1)
+
+    def top2():
+        return vpa.top_tokens(x2, w2.vocab, w2.shard_width, w2.n_shards, 8192, workspace=ws2)
+
+    def verify3(drafts=d3):
+        st = vpa.verify_stats(x3, w3.vocab, w3.shard_width, w3.n_shards, w3.n_req, w3.k)
+        return vpa.greedy_verify(st[0], st[1], drafts, with_targets=False)
+
+    md3, mb3 = slots(w3.shard_width, w3.n_shards, 8192), slots(w3.shard_width, w3.n_shards, 1024)
+    cfg_bytes = {
+        "config1": top_tokens_bytes(4, w1.vocab, 4, w1.n_shards,
+                                    slots(w1.shard_width, w1.n_shards, 256)),
+        "config2": top_tokens_bytes(32, w2.vocab, 2, w2.n_shards,
+                                    slots(w2.shard_width, w2.n_shards, 8192)),
+        "config3": verify_bytes(w3.n_req, w3.k, w3.vocab, 2, w3.n_shards, md3, mb3),
+    }
+    cfg_desc = {
+        "config1": "top_tokens, 4 x 1000 fp32, 1 shard, B=256",
+        "config2": "top_tokens, 32 x 151936 bf16 padded to 152064, 2 shards, B=8192",
+        "config3": ("verify_stats + greedy_verify, 24 requests x (K=3 + 1) rows x 200064 bf16, "
+                    "4 shards, B=8192/1024"),
+    }
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        verify3()
-        vpa.top_tokens(x2, w2.vocab, w2.shard_width, w2.n_shards, 8192, workspace=ws2)
+    with torch.cuda.stream(side):                # warm the allocator off the capture stream
+        top1(), top2(), verify3()
     torch.cuda.current_stream().wait_stream(side)
-    g_small = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_small):
-        vpa.top_tokens(x2, w2.vocab, w2.shard_width, w2.n_shards, 8192, workspace=ws2)
-        verify3()
-    small["graph_top_tokens_32_plus_verify_24x4"] = per_call(g_small.replay) * 1e6
-    # each alone, replayed from a graph of 20 back-to-back copies: the GPU
-    # time of one decode-sized call
-    for name, fn in (("graph_top_tokens_32x151936_s2",
-                      lambda: vpa.top_tokens(x2, w2.vocab, w2.shard_width, w2.n_shards, 8192,
-                                             workspace=ws2)),
-                     ("graph_verify_24x4_rows_200064_s4", verify3)):
+    per_config = {}
+    for name, fn in (("config1", top1), ("config2", top2), ("config3", verify3)):
+        settle(fn)
+        eager = per_call(fn)
         g_one = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_one):
             for _ in range(20):
                 fn()
-        small[name] = per_call(g_one.replay) / 20 * 1e6
-    result["small_configs_us"] = small
+        settle(g_one.replay)
+        graph = per_call(g_one.replay) / 20
+        per_config[name] = {
+            "calls": cfg_desc[name], "eager_us": eager * 1e6, "graph_us": graph * 1e6,
+            "eager_over_graph": eager / graph, "algorithmic_bytes": cfg_bytes[name],
+            "gbps_graph": cfg_bytes[name] / graph / 1e9,
+            "hbm_frac_graph": cfg_bytes[name] / graph / 1e9 / PEAK_HBM_GBPS,
+        }
+    g_small = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_small):
+        top2()
+        verify3()
+    settle(g_small.replay)
+    per_config["graph_config2_plus_config3_us"] = per_call(g_small.replay) * 1e6
+    result["per_config"] = per_config
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         torch.cuda.synchronize()
         gpu_out = (ids.cpu(), vals.cpu(), out.cpu(), ns.cpu(), nr.cpu())
         result["cpu_baseline"] = cpu_baseline(xd.cpu(), xt[:R * (K + 1)].cpu(), drafts_cpu,
                                               gpu_out)
+        result["cpu_baseline"]["per_config"] = oracle_per_config(
+            (w1, w2, w3), {"config1": top1, "config2": top2, "config3": verify3}, cfg_bytes, dev)
     print(json.dumps(result), flush=True)
 
 

@@ -1,6 +1,8 @@
-"""ctypes binding of libvpa_probe.so (include/vpa_probe.h): the HBM
-read-ceiling probe that the benchmark reports beside the statistics kernel's
-roofline.  Measurement only; the argmax path never loads it."""
+"""hbm_probe -- the HBM read-ceiling probe that bench.py reports beside the
+statistics kernel's roofline: a ctypes binding of libvpa_probe.so
+(hbm_probe/vpa_probe.h, built from hbm_probe/read_probe.hip by
+hbm_probe/build.py).  Measurement only: the argmax library neither contains
+nor calls it, and only bench.py and tests/test_read_probe.py load it."""
 import ctypes
 import os
 

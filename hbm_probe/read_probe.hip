@@ -1,6 +1,7 @@
 // read_probe.hip -- the practical HBM read ceiling, for reporting beside the
 // statistics kernel's roofline.  Not part of the argmax path: libvpa_probe.so
-// is built from this file alone and only the benchmark and its test load it.
+// is built from this file alone (hbm_probe/build.py) and only the benchmark
+// and its test load it.
 //
 // A persistent grid of 256-thread workgroups walks the buffer in 4 KiB chunks
 // (one chunk = four 1 KiB wavefront-wide loads, 16-byte non-temporal loads

@@ -1,4 +1,4 @@
-"""The HBM read-ceiling probe (include/vpa_probe.h, libvpa_probe.so): on the
+"""The HBM read-ceiling probe (hbm_probe/vpa_probe.h, libvpa_probe.so): on the
 CPU, its exports, header and argument checks; on the GPU, that one call reads
 every byte of the read range exactly once (the XOR of the sink equals the
 XOR of the range's 32-bit words, computed with numpy)."""
@@ -12,9 +12,9 @@ import numpy as np
 import pytest
 import torch
 
-from vocab_argmax_amd import read_probe
+import hbm_probe as read_probe
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "hbm_probe",
                       "vpa_probe.h")
 FAKE = ctypes.c_void_p(0x10000)
 

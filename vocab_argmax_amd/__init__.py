@@ -326,6 +326,7 @@ def combine_stats(stats, d2t=None, scale=1.0, *, stream=None):
     return (ids, vals) if d2t is None else (ids, vals, mapped)
 
 
+@functools.lru_cache(maxsize=256)
 def top_tokens_workspace(vocab, shard_width, n_shards, n_rows, block=DRAFT_BLOCK) -> int:
     return int(lib().vpa_top_tokens_workspace(_vocab(vocab, shard_width, n_shards), n_rows, block))
 
@@ -344,8 +345,15 @@ def top_tokens(logits, vocab, shard_width, n_shards, block=DRAFT_BLOCK, workspac
     n = logits.shape[0]
     dev = logits.device
     voc = _vocab(vocab, shard_width, n_shards)
-    if workspace is None:
-        need = int(lib().vpa_top_tokens_workspace(voc, n, block))
+    if workspace is None and ids is None and val_bits is None:
+        # one allocation: the workspace, then ids and value bits
+        need = (top_tokens_workspace(vocab, shard_width, n_shards, n, block) + 255) // 256 * 256
+        buf = torch.empty(need + 8 * n, dtype=torch.uint8, device=dev)
+        workspace = buf[:max(need, 8)]
+        outs = buf[need:].view(torch.int32)
+        ids, val_bits = outs[:n], outs[n:]
+    elif workspace is None:
+        need = top_tokens_workspace(vocab, shard_width, n_shards, n, block)
         workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=dev)
     elif not workspace.is_contiguous() or workspace.device != dev:
         raise ValueError(f"workspace must be a contiguous tensor on {dev}")

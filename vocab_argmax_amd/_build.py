@@ -5,9 +5,6 @@
 Sources are compiled in parallel into vocab_argmax_amd/_build/ and linked into
 vocab_argmax_amd/libvpa.so.  Packed-fp32 instructions are disabled for the
 device code (the path has no float arithmetic; the flag keeps it that way).
-The HBM read-ceiling probe (csrc/read_probe.hip, include/vpa_probe.h) is
-built on its own into vocab_argmax_amd/libvpa_probe.so: only the benchmark
-and its test load it.
 """
 import os
 import shutil
@@ -21,8 +18,6 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libvpa.so")
 SOURCES = ["api.hip", "block_stats.hip", "reduce.hip"]
-PROBE_LIB = os.path.join(PKG, "libvpa_probe.so")
-PROBE_SOURCES = ["read_probe.hip"]
 ARCH = "gfx950"
 
 
@@ -64,10 +59,9 @@ def build(verbose: bool = False, extra_flags=()) -> str:
             raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
         os.replace(out + ".tmp", out)
 
-    with ThreadPoolExecutor(max_workers=len(SOURCES) + len(PROBE_SOURCES)) as ex:
-        objs = list(ex.map(one, SOURCES + PROBE_SOURCES))
-    link(objs[:len(SOURCES)], LIB)
-    link(objs[len(SOURCES):], PROBE_LIB)
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(one, SOURCES))
+    link(objs, LIB)
     return LIB
 
 

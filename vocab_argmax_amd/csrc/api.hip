@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <string.h>
 
 #include <atomic>
 #include <mutex>
@@ -41,7 +42,18 @@ vpa_status ok() {
     return VPA_OK;
 }
 
-int esize_of(vpa_dtype dt) {
+// The dtype argument's integer value.  A C caller may pass any int as a
+// vpa_dtype, but in C++ loading an enum outside the range of its
+// enumerators is undefined (even to pass it on), so every entry point reads
+// its dtype argument's bytes as an int first and works with that int.
+int dtype_value(const vpa_dtype* dt) {
+    static_assert(sizeof(vpa_dtype) == sizeof(int), "vpa_dtype is int-sized");
+    int raw;
+    memcpy(&raw, dt, sizeof raw);
+    return raw;
+}
+
+int esize_of(int dt) {
     return dt == VPA_BF16 ? 2 : (dt == VPA_F32 ? 4 : 0);
 }
 
@@ -78,14 +90,14 @@ vpa_status check_vocab(const vpa_vocab& v) {
     return ok();
 }
 
-vpa_status check_dtype(vpa_dtype dt) {
+vpa_status check_dtype(int dt) {
     if (esize_of(dt) == 0)
-        return fail(VPA_ERR_UNSUPPORTED, "dtype %d is not VPA_F32 or VPA_BF16", (int)dt);
+        return fail(VPA_ERR_UNSUPPORTED, "dtype %d is not VPA_F32 or VPA_BF16", dt);
     return ok();
 }
 
 // Shared checks of the logits-reading calls; fills `t` with the geometry.
-vpa_status check_logits_task(vpa_dtype dt, int64_t ld, const vpa_vocab& v, int32_t first_shard,
+vpa_status check_logits_task(int dt, int64_t ld, const vpa_vocab& v, int32_t first_shard,
                              int32_t n_local, int32_t block, vpa::SegTask& t) {
     vpa_status st;
     if ((st = check_dtype(dt)) != VPA_OK)
@@ -120,7 +132,7 @@ vpa_status check_logits_task(vpa_dtype dt, int64_t ld, const vpa_vocab& v, int32
 
 // Pointer checks of the logits, made only when there is work (an empty batch
 // may pass the NULL data pointer of an empty tensor).
-vpa_status check_logits_ptr(const void* logits, vpa_dtype dt) {
+vpa_status check_logits_ptr(const void* logits, int dt) {
     if (!logits)
         return fail(VPA_ERR_INVALID, "logits is NULL");
     if (!aligned(logits, (size_t)esize_of(dt)))
@@ -192,7 +204,7 @@ struct TopCall {
     int esize;
 };
 
-vpa_status check_top_tokens(const void* logits, vpa_dtype dtype, int64_t ld, const vpa_vocab& v,
+vpa_status check_top_tokens(const void* logits, int dtype, int64_t ld, const vpa_vocab& v,
                             int64_t n_rows, int32_t block, const vpa_epilogue* epi,
                             const int32_t* ids, const uint32_t* val_bits, int64_t* mapped,
                             TopCall& c) {
@@ -280,8 +292,9 @@ vpa_status vpa_block_stats(const void* logits, vpa_dtype dtype, int64_t ld, vpa_
                            int32_t first_shard, int32_t n_local_shards, const int32_t* rows,
                            int64_t n_rows, int64_t logits_rows, int32_t block, vpa_stat* stats,
                            void* stream) {
+    const int dt = dtype_value(&dtype);
     vpa::SegTask t;
-    vpa_status st = check_logits_task(dtype, ld, v, first_shard, n_local_shards, block, t);
+    vpa_status st = check_logits_task(dt, ld, v, first_shard, n_local_shards, block, t);
     if (st != VPA_OK)
         return st;
     if (n_rows < 0)
@@ -292,7 +305,7 @@ vpa_status vpa_block_stats(const void* logits, vpa_dtype dtype, int64_t ld, vpa_
         return st;
     if (n_rows == 0)
         return ok();
-    if ((st = check_logits_ptr(logits, dtype)) != VPA_OK)
+    if ((st = check_logits_ptr(logits, dt)) != VPA_OK)
         return st;
     if (!stats || !aligned(stats, 8))
         return fail(VPA_ERR_INVALID, "stats is NULL or not 8-byte aligned");
@@ -303,10 +316,10 @@ vpa_status vpa_block_stats(const void* logits, vpa_dtype dtype, int64_t ld, vpa_
     t.logits_rows = logits_rows;
     t.stats = stats;
     vpa::SegTask none{};
-    if ((st = check_dispatch(vpa::block_stats_threads(esize_of(dtype), t, none),
+    if ((st = check_dispatch(vpa::block_stats_threads(esize_of(dt), t, none),
                              "vpa_block_stats")) != VPA_OK)
         return st;
-    hipError_t e = vpa::launch_block_stats(esize_of(dtype), t, none, (hipStream_t)stream);
+    hipError_t e = vpa::launch_block_stats(esize_of(dt), t, none, (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "vpa_block_stats launch");
 }
 
@@ -314,15 +327,16 @@ vpa_status vpa_verify_stats(const void* logits, vpa_dtype dtype, int64_t ld, vpa
                             int32_t first_shard, int32_t n_local_shards, int64_t n_req, int32_t k,
                             int32_t block_draft, int32_t block_bonus, vpa_stat* draft_stats,
                             vpa_stat* bonus_stats, void* stream) {
+    const int dt = dtype_value(&dtype);
     vpa::SegTask td, tb;
     vpa_status st;
-    if ((st = check_logits_task(dtype, ld, v, first_shard, n_local_shards, block_draft, td)) != VPA_OK)
+    if ((st = check_logits_task(dt, ld, v, first_shard, n_local_shards, block_draft, td)) != VPA_OK)
         return st;
-    if ((st = check_logits_task(dtype, ld, v, first_shard, n_local_shards, block_bonus, tb)) != VPA_OK)
+    if ((st = check_logits_task(dt, ld, v, first_shard, n_local_shards, block_bonus, tb)) != VPA_OK)
         return st;
     if (k < 1 || k > VPA_MAX_DRAFTS)
         return fail(VPA_ERR_INVALID, "k %d outside [1, %d]", (int)k, VPA_MAX_DRAFTS);
-    if (n_req < 0 || n_req * (int64_t)(k + 1) > INT32_MAX)
+    if (n_req < 0 || n_req > INT32_MAX / (k + 1))   // n_req * (k+1) <= 2^31-1, no overflow
         return fail(VPA_ERR_INVALID, "n_req %lld out of range", (long long)n_req);
     if ((st = set_items(td, n_req * k, "vpa_verify_stats (draft rows)")) != VPA_OK)
         return st;
@@ -332,7 +346,7 @@ vpa_status vpa_verify_stats(const void* logits, vpa_dtype dtype, int64_t ld, vpa
         return fail(VPA_ERR_INVALID, "vpa_verify_stats: too many statistics per call");
     if (n_req == 0)
         return ok();
-    if ((st = check_logits_ptr(logits, dtype)) != VPA_OK)
+    if ((st = check_logits_ptr(logits, dt)) != VPA_OK)
         return st;
     if (!draft_stats || !bonus_stats || !aligned(draft_stats, 8) || !aligned(bonus_stats, 8))
         return fail(VPA_ERR_INVALID, "draft_stats/bonus_stats NULL or not 8-byte aligned");
@@ -346,10 +360,10 @@ vpa_status vpa_verify_stats(const void* logits, vpa_dtype dtype, int64_t ld, vpa
     tb.row_bonus = 1;
     tb.logits_rows = logits_rows;
     tb.stats = bonus_stats;
-    if ((st = check_dispatch(vpa::block_stats_threads(esize_of(dtype), td, tb),
+    if ((st = check_dispatch(vpa::block_stats_threads(esize_of(dt), td, tb),
                              "vpa_verify_stats")) != VPA_OK)
         return st;
-    hipError_t e = vpa::launch_block_stats(esize_of(dtype), td, tb, (hipStream_t)stream);
+    hipError_t e = vpa::launch_block_stats(esize_of(dt), td, tb, (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "vpa_verify_stats launch");
 }
 
@@ -359,11 +373,12 @@ vpa_status vpa_verify_stats_rows(const void* logits, vpa_dtype dtype, int64_t ld
                                  const int32_t* bonus_rows, int64_t n_bonus_rows,
                                  int64_t logits_rows, int32_t block_draft, int32_t block_bonus,
                                  vpa_stat* draft_stats, vpa_stat* bonus_stats, void* stream) {
+    const int dt = dtype_value(&dtype);
     vpa::SegTask td, tb;
     vpa_status st;
-    if ((st = check_logits_task(dtype, ld, v, first_shard, n_local_shards, block_draft, td)) != VPA_OK)
+    if ((st = check_logits_task(dt, ld, v, first_shard, n_local_shards, block_draft, td)) != VPA_OK)
         return st;
-    if ((st = check_logits_task(dtype, ld, v, first_shard, n_local_shards, block_bonus, tb)) != VPA_OK)
+    if ((st = check_logits_task(dt, ld, v, first_shard, n_local_shards, block_bonus, tb)) != VPA_OK)
         return st;
     if (n_draft_rows < 0 || n_bonus_rows < 0 || logits_rows < 0)
         return fail(VPA_ERR_INVALID, "negative row count");
@@ -375,7 +390,7 @@ vpa_status vpa_verify_stats_rows(const void* logits, vpa_dtype dtype, int64_t ld
         return fail(VPA_ERR_INVALID, "vpa_verify_stats_rows: too many statistics per call");
     if (n_draft_rows == 0 && n_bonus_rows == 0)
         return ok();
-    if ((st = check_logits_ptr(logits, dtype)) != VPA_OK)
+    if ((st = check_logits_ptr(logits, dt)) != VPA_OK)
         return st;
     if ((n_draft_rows && (!draft_rows || !aligned(draft_rows, 4) || !draft_stats ||
                           !aligned(draft_stats, 8))) ||
@@ -389,16 +404,16 @@ vpa_status vpa_verify_stats_rows(const void* logits, vpa_dtype dtype, int64_t ld
     tb.rows = bonus_rows;
     tb.logits_rows = logits_rows;
     tb.stats = bonus_stats;
-    if ((st = check_dispatch(vpa::block_stats_threads(esize_of(dtype), td, tb),
+    if ((st = check_dispatch(vpa::block_stats_threads(esize_of(dt), td, tb),
                              "vpa_verify_stats_rows")) != VPA_OK)
         return st;
-    hipError_t e = vpa::launch_block_stats(esize_of(dtype), td, tb, (hipStream_t)stream);
+    hipError_t e = vpa::launch_block_stats(esize_of(dt), td, tb, (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "vpa_verify_stats_rows launch");
 }
 
 vpa_status vpa_ragged_rows(const int32_t* cu, int64_t n_req, int64_t total_drafts,
                            int32_t* draft_rows, int32_t* bonus_rows, void* stream) {
-    if (n_req < 0 || total_drafts < 0 || total_drafts + n_req > INT32_MAX)
+    if (n_req < 0 || total_drafts < 0 || n_req > INT32_MAX || total_drafts > INT32_MAX - n_req)
         return fail(VPA_ERR_INVALID, "n_req %lld / total_drafts %lld out of range",
                     (long long)n_req, (long long)total_drafts);
     if (n_req == 0)
@@ -455,8 +470,9 @@ vpa_status vpa_top_tokens(const void* logits, vpa_dtype dtype, int64_t ld, vpa_v
                           int64_t n_rows, int32_t block, void* workspace, size_t workspace_bytes,
                           const vpa_epilogue* epi, int32_t* ids, uint32_t* val_bits,
                           int64_t* mapped, void* stream) {
+    const int dt = dtype_value(&dtype);
     TopCall c;
-    vpa_status st = check_top_tokens(logits, dtype, ld, v, n_rows, block, epi, ids, val_bits,
+    vpa_status st = check_top_tokens(logits, dt, ld, v, n_rows, block, epi, ids, val_bits,
                                      mapped, c);
     if (st != VPA_OK || n_rows == 0)
         return st;
@@ -470,8 +486,9 @@ vpa_status vpa_top_tokens_noalloc(const void* logits, vpa_dtype dtype, int64_t l
                                   int64_t n_rows, int32_t block, const vpa_epilogue* epi,
                                   int32_t* ids, uint32_t* val_bits, int64_t* mapped,
                                   void* stream) {
+    const int dt = dtype_value(&dtype);
     TopCall c;
-    vpa_status st = check_top_tokens(logits, dtype, ld, v, n_rows, block, epi, ids, val_bits,
+    vpa_status st = check_top_tokens(logits, dt, ld, v, n_rows, block, epi, ids, val_bits,
                                      mapped, c);
     if (st != VPA_OK || n_rows == 0)
         return st;
@@ -497,7 +514,7 @@ vpa_status vpa_greedy_verify(const vpa_stat* draft_stats, int32_t m_draft,
                     (int)n_shards, (int)m_draft, (int)m_bonus);
     if (k < 1 || k > VPA_MAX_DRAFTS)
         return fail(VPA_ERR_INVALID, "k %d outside [1, %d]", (int)k, VPA_MAX_DRAFTS);
-    if (n_req < 0 || n_req * (int64_t)(k + 1) > INT32_MAX)
+    if (n_req < 0 || n_req > INT32_MAX / (k + 1))   // n_req * (k+1) <= 2^31-1, no overflow
         return fail(VPA_ERR_INVALID, "n_req %lld out of range", (long long)n_req);
     if (n_req == 0)
         return ok();
@@ -530,7 +547,7 @@ vpa_status vpa_greedy_verify_ragged(const vpa_stat* draft_stats, int32_t m_draft
         (int64_t)n_shards * m_bonus > INT32_MAX)
         return fail(VPA_ERR_INVALID, "n_shards %d / m_draft %d / m_bonus %d invalid",
                     (int)n_shards, (int)m_draft, (int)m_bonus);
-    if (n_req < 0 || total_drafts < 0 || total_drafts + n_req > INT32_MAX)
+    if (n_req < 0 || total_drafts < 0 || n_req > INT32_MAX || total_drafts > INT32_MAX - n_req)
         return fail(VPA_ERR_INVALID, "n_req %lld / total_drafts %lld out of range",
                     (long long)n_req, (long long)total_drafts);
     if (n_req == 0)
