@@ -275,10 +275,10 @@ def verify_stats(logits, vocab, shard_width, n_shards, n_req, k, block_draft=DRA
     mb = stats_slots(shard_width, n_shards, block_bonus)
     if out is None:
         # one allocation for both: draft statistics first, then bonus statistics
-        nd = n_local * n_req * k * md * 2
-        buf = torch.empty(nd + n_local * n_req * mb * 2, dtype=torch.int32, device=dev)
-        dst = buf[:nd].view(n_local, n_req * k, md, 2)
-        bst = buf[nd:].view(n_local, n_req, mb, 2)
+        nd, nb = n_local * n_req * k * md * 2, n_local * n_req * mb * 2
+        buf = torch.empty(nd + nb, dtype=torch.int32, device=dev)
+        dst = buf.as_strided((n_local, n_req * k, md, 2), (n_req * k * md * 2, md * 2, 2, 1), 0)
+        bst = buf.as_strided((n_local, n_req, mb, 2), (n_req * mb * 2, mb * 2, 2, 1), nd)
     else:
         dst, bst = out
         if (tuple(dst.shape) != (n_local, n_req * k, md, 2)
@@ -317,8 +317,8 @@ def combine_stats(stats, d2t=None, scale=1.0, *, stream=None):
     _stats_tensor(stats, "stats")
     s, n, m, _ = stats.shape
     dev = stats.device
-    buf = torch.empty((2, n), dtype=torch.int32, device=dev)
-    ids, vals = buf[0], buf[1]
+    buf = torch.empty(2 * n, dtype=torch.int32, device=dev)
+    ids, vals = buf.as_strided((n,), (1,), 0), buf.as_strided((n,), (1,), n)
     mapped = torch.empty(n, dtype=torch.int64, device=dev) if d2t is not None else None
     epi, _keep = _epilogue(d2t, scale, dev)
     _check(_on(dev, lib().vpa_combine_stats, stats.data_ptr(), s, n, m, epi, ids.data_ptr(),
@@ -346,33 +346,35 @@ def top_tokens(logits, vocab, shard_width, n_shards, block=DRAFT_BLOCK, workspac
     dev = logits.device
     voc = _vocab(vocab, shard_width, n_shards)
     if workspace is None and ids is None and val_bits is None:
-        # one allocation: the workspace, then ids and value bits
-        need = (top_tokens_workspace(vocab, shard_width, n_shards, n, block) + 255) // 256 * 256
-        buf = torch.empty(need + 8 * n, dtype=torch.uint8, device=dev)
-        workspace = buf[:max(need, 8)]
-        outs = buf[need:].view(torch.int32)
-        ids, val_bits = outs[:n], outs[n:]
-    elif workspace is None:
-        need = top_tokens_workspace(vocab, shard_width, n_shards, n, block)
-        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=dev)
-    elif not workspace.is_contiguous() or workspace.device != dev:
-        raise ValueError(f"workspace must be a contiguous tensor on {dev}")
-    if ids is None and val_bits is None:
-        buf = torch.empty((2, n), dtype=torch.int32, device=dev)
-        ids, val_bits = buf[0], buf[1]
+        # one int32 allocation: the workspace (rounded up to 256 bytes), then
+        # ids, then value bits
+        need = (top_tokens_workspace(vocab, shard_width, n_shards, n, block) + 255) // 256 * 64
+        buf = torch.empty(need + 2 * n, dtype=torch.int32, device=dev)
+        ws_ptr, ws_bytes = buf.data_ptr(), 4 * need
+        ids = buf.as_strided((n,), (1,), need)
+        val_bits = buf.as_strided((n,), (1,), need + n)
     else:
-        ids = (torch.empty(n, dtype=torch.int32, device=dev) if ids is None
-               else _out_tensor(ids, "ids", torch.int32, n, dev))
-        val_bits = (torch.empty(n, dtype=torch.int32, device=dev) if val_bits is None
-                    else _out_tensor(val_bits, "val_bits", torch.int32, n, dev))
+        if workspace is None:
+            need = top_tokens_workspace(vocab, shard_width, n_shards, n, block)
+            workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=dev)
+        elif not workspace.is_contiguous() or workspace.device != dev:
+            raise ValueError(f"workspace must be a contiguous tensor on {dev}")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        if ids is None and val_bits is None:
+            buf = torch.empty(2 * n, dtype=torch.int32, device=dev)
+            ids, val_bits = buf.as_strided((n,), (1,), 0), buf.as_strided((n,), (1,), n)
+        else:
+            ids = (torch.empty(n, dtype=torch.int32, device=dev) if ids is None
+                   else _out_tensor(ids, "ids", torch.int32, n, dev))
+            val_bits = (torch.empty(n, dtype=torch.int32, device=dev) if val_bits is None
+                        else _out_tensor(val_bits, "val_bits", torch.int32, n, dev))
     if d2t is not None:
         mapped = (torch.empty(n, dtype=torch.int64, device=dev) if mapped is None
                   else _out_tensor(mapped, "mapped", torch.int64, n, dev))
     epi, _keep = _epilogue(d2t, scale, dev)
     _check(_on(dev, lib().vpa_top_tokens, logits.data_ptr(), _dtype_code(logits), ld, voc, n,
-               block, workspace.data_ptr(), workspace.numel() * workspace.element_size(), epi,
-               ids.data_ptr(), val_bits.data_ptr(), _vp(mapped if d2t is not None else None),
-               _stream(stream, dev)))
+               block, ws_ptr, ws_bytes, epi, ids.data_ptr(), val_bits.data_ptr(),
+               _vp(mapped if d2t is not None else None), _stream(stream, dev)))
     return (ids, val_bits) if d2t is None else (ids, val_bits, mapped)
 
 
@@ -389,8 +391,8 @@ def top_tokens_noalloc(logits, vocab, shard_width, n_shards, block=DRAFT_BLOCK, 
     n = logits.shape[0]
     dev = logits.device
     if ids is None and val_bits is None:
-        buf = torch.empty((2, n), dtype=torch.int32, device=dev)
-        ids, val_bits = buf[0], buf[1]
+        buf = torch.empty(2 * n, dtype=torch.int32, device=dev)
+        ids, val_bits = buf.as_strided((n,), (1,), 0), buf.as_strided((n,), (1,), n)
     else:
         ids = (torch.empty(n, dtype=torch.int32, device=dev) if ids is None
                else _out_tensor(ids, "ids", torch.int32, n, dev))
@@ -411,12 +413,14 @@ def _verify_outputs(r, k, with_targets, dev):
     """out_tokens [r][k+1], num_sampled [r], num_rejected [r] and, if asked for,
     target_ids [r][k+1], as views of one int32 allocation."""
     per = r * (k + 1)
-    buf = torch.empty(per * (2 if with_targets else 1) + 2 * r, dtype=torch.int32, device=dev)
-    out_t = buf[:per].view(r, k + 1)
-    ns = buf[per:per + r]
-    nr = buf[per + r:per + 2 * r]
-    tg = buf[per + 2 * r:].view(r, k + 1) if with_targets else None
-    return out_t, ns, nr, tg
+    if with_targets:
+        buf = torch.empty(2 * per + 2 * r, dtype=torch.int32, device=dev)
+        ns, nr = buf.split_with_sizes((2 * per, r, r))[1:]
+        return (buf.as_strided((r, k + 1), (k + 1, 1), 0), ns, nr,
+                buf.as_strided((r, k + 1), (k + 1, 1), per))
+    buf = torch.empty(per + 2 * r, dtype=torch.int32, device=dev)
+    ns, nr = buf.split_with_sizes((per, r, r))[1:]
+    return buf.as_strided((r, k + 1), (k + 1, 1), 0), ns, nr, None
 
 
 @_stream_arg

@@ -25,22 +25,39 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kVerifyMaxThreads = 1024;
 
 // Best statistic of row `row` of a [S][rows_total][m] array; every lane
-// returns the same (id, bits).
+// returns the same (id, bits).  A lane's statistics are loaded kRowBatch at a
+// time before any is compared, so a row of up to 64*kRowBatch statistics
+// (the bonus rows' 1024-column blocks: 200-208 of them) costs one memory
+// round trip, not one per 64.
+constexpr int kRowBatch = 4;
+
 __device__ __forceinline__ void row_best(const vpa_stat* __restrict__ stats, int32_t n_shards,
                                          int64_t rows_total, int64_t row, int32_t m, int lane,
                                          int32_t& id, uint32_t& bits) {
     uint32_t bk = 0, bn = 0, bb = 0;
     const int32_t total = n_shards * m;
-    for (int32_t idx = lane; idx < total; idx += 64) {
-        const int32_t s = idx / m;
-        const int32_t j = idx - s * m;
-        const vpa_stat st = stats[((int64_t)s * rows_total + row) * m + j];
-        const uint32_t k = key_f32(st.val_bits);
-        const uint32_t n = ~(uint32_t)st.id;
-        if (k > bk || (k == bk && n > bn)) {
-            bk = k;
-            bn = n;
-            bb = st.val_bits;
+    for (int32_t i0 = lane; i0 < total; i0 += 64 * kRowBatch) {
+        vpa_stat st[kRowBatch];
+#pragma unroll
+        for (int u = 0; u < kRowBatch; ++u) {
+            const int32_t idx = i0 + 64 * u;
+            if (idx < total) {
+                const int32_t s = idx / m;
+                const int32_t j = idx - s * m;
+                st[u] = stats[((int64_t)s * rows_total + row) * m + j];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kRowBatch; ++u) {
+            if (i0 + 64 * u >= total)
+                break;
+            const uint32_t k = key_f32(st[u].val_bits);
+            const uint32_t n = ~(uint32_t)st[u].id;
+            if (k > bk || (k == bk && n > bn)) {
+                bk = k;
+                bn = n;
+                bb = st[u].val_bits;
+            }
         }
     }
     wave_best_stat(bk, bn, bb);
