@@ -13,13 +13,54 @@ import bruteforce as bf
 import vocab_argmax_amd as vpa
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "vpa.h")
-FAKE = ctypes.c_void_p(0x10000)     # aligned, never dereferenced by a rejected call
-FAKE_ODD = ctypes.c_void_p(0x10001)
+# aligned, never dereferenced by a rejected call; above 2^32, so that an
+# address passed through a 32-bit slot fails loudly
+FAKE = ctypes.c_void_p(0x7F0000010000)
+FAKE_ODD = ctypes.c_void_p(0x7F0000010001)
 
 
-@pytest.fixture(scope="module")
-def lib():
-    return vpa.lib()
+def _as_python(arg):
+    """One ctypes argument as the _vpa_call module takes it (a list: a vocab
+    struct becomes three ints)."""
+    if isinstance(arg, ctypes.c_void_p):
+        return [arg.value]
+    if isinstance(arg, vpa.Vocab):
+        return [arg.vocab, arg.shard_width, arg.n_shards]
+    if isinstance(arg, ctypes.POINTER(vpa.Epilogue)):
+        e = arg.contents
+        return [(e.d2t, e.d2t_len, e.scale)]
+    return [arg]
+
+
+class BothPaths:
+    """The loaded library, whose launch entry points run twice: through ctypes
+    and through the binding's _vpa_call module.  Both must return the same
+    status and, on an error, the same message."""
+
+    def __init__(self, loaded):
+        self._lib = loaded
+
+    def __getattr__(self, name):
+        through_ctypes = getattr(self._lib, name)
+        if name not in vpa.call().entries():
+            return through_ctypes
+        through_module = getattr(vpa.call(), name)
+
+        def both(*args):
+            st = through_ctypes(*args)
+            msg = vpa.last_error() if st != vpa.VPA_OK else ""
+            st2 = through_module(*[a for arg in args for a in _as_python(arg)])
+            msg2 = vpa.last_error() if st2 != vpa.VPA_OK else ""
+            assert (st2, msg2) == (st, msg), f"{name}: _vpa_call and ctypes disagree"
+            return st
+        return both
+
+
+@pytest.fixture(scope="module", params=["ctypes", "ctypes_and_module"])
+def lib(request):
+    """Every C-ABI test runs on the library through ctypes, then once more
+    with each launch also made through the binding's _vpa_call module."""
+    return vpa.lib() if request.param == "ctypes" else BothPaths(vpa.lib())
 
 
 def declared_functions():
@@ -320,3 +361,45 @@ def test_noalloc_top_tokens_rejects_beyond_its_array(lib):
     assert call(4, block=0) == vpa.VPA_ERR_INVALID
     assert lib.vpa_top_tokens_noalloc(FAKE, vpa.VPA_BF16, 200064, voc, 4, 8192,
                                       EPI(scale=-1.0), FAKE, None, None, None) == vpa.VPA_ERR_INVALID
+
+
+def test_module_covers_every_launch_entry_point():
+    """_vpa_call marshals every entry point that enqueues work; the three
+    host-only queries stay on ctypes."""
+    host_only = {"vpa_stats_slots", "vpa_top_tokens_workspace", "vpa_last_error"}
+    assert set(vpa.call().entries()) == set(vpa.SYMBOLS) - host_only
+
+
+def test_module_rejects_bad_python_arguments():
+    """Arguments the C types cannot hold raise before the library is called."""
+    c = vpa.call()
+    ok = (0x10000, vpa.VPA_BF16, 1000, 1000, 125, 8, 0, 256, None, 0, None, None, None, None, 0)
+    assert c.vpa_top_tokens(*ok) == vpa.VPA_OK              # zero rows: nothing enqueued
+    with pytest.raises(TypeError, match="takes 15 arguments"):
+        c.vpa_top_tokens(*ok[:-1])
+    with pytest.raises(OverflowError):                    # block is an int32
+        c.vpa_top_tokens(*ok[:7], 1 << 31, *ok[8:])
+    with pytest.raises(OverflowError):                    # addresses are unsigned
+        c.vpa_top_tokens(-1, *ok[1:])
+    with pytest.raises(TypeError):
+        c.vpa_top_tokens(0x10000, vpa.VPA_BF16, 1000.0, *ok[3:])
+    with pytest.raises(TypeError, match="epilogue"):
+        c.vpa_top_tokens(*ok[:10], (None, 0), *ok[11:])
+    with pytest.raises(TypeError):
+        c.vpa_top_tokens(*ok[:10], (None, 0, "x"), *ok[11:])
+    with pytest.raises(KeyError):
+        c.bind("vpa_no_such_entry", 0x10000)
+    with pytest.raises(ValueError):
+        c.bind("vpa_top_tokens", 0)
+
+
+def test_module_passes_scale_as_fp32():
+    """A scale that rounds to zero as an fp32 is rejected as zero, as a C float
+    argument would be."""
+    c = vpa.call()
+    args = (0x10000, vpa.VPA_BF16, 1000, 1000, 125, 8, 0, 256, None, 0, (None, 0, 1e-46),
+            None, None, None, 0)
+    assert c.vpa_top_tokens(*args) == vpa.VPA_ERR_INVALID
+    assert "scale" in vpa.last_error()
+    args = args[:10] + ((None, 0, 2.0 ** -149),) + args[11:]   # the least fp32 subnormal
+    assert c.vpa_top_tokens(*args) == vpa.VPA_OK

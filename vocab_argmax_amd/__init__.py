@@ -1,9 +1,13 @@
 """vocab_argmax_amd -- vocab-parallel greedy argmax and greedy verification on
 MI355X (gfx950).
 
-A thin ctypes binding over libvpa.so, whose C ABI is include/vpa.h.  This
-module only marshals arguments: it checks devices, dtypes and strides, passes
-``data_ptr()`` and the current HIP stream, and allocates outputs with torch.
+A thin binding over libvpa.so, whose C ABI is include/vpa.h.  ctypes loads
+the library; the launch entry points are called through _vpa_call, a small
+CPython module (csrc/pycall.c) bound to that same loaded library, which
+converts Python ints to C arguments at a fraction of ctypes' per-call cost.
+This module only marshals arguments: it checks devices, dtypes and strides,
+passes ``data_ptr()`` and the current HIP stream, and allocates outputs with
+torch.
 Every step of the computation runs in the library's HIP kernels; there is no
 fallback.  If libvpa.so is missing, every call raises.
 
@@ -60,6 +64,7 @@ class Epilogue(ctypes.Structure):
 
 
 _lib = None
+_call_mod = None
 
 
 def _bind(lib):
@@ -106,8 +111,33 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m vocab_argmax_amd._build` (hipcc, gfx950)")
-        _lib = _bind(ctypes.CDLL(LIB_PATH))
+        loaded = _bind(ctypes.CDLL(LIB_PATH))
+        _bind_call(loaded)
+        _lib = loaded
     return _lib
+
+
+def _bind_call(loaded):
+    """Point _vpa_call's entry points at the library just loaded."""
+    global _call_mod
+    try:
+        from . import _vpa_call
+    except ImportError as e:
+        raise RuntimeError("vocab_argmax_amd/_vpa_call is missing: build it with "
+                           f"`python -m vocab_argmax_amd._build` ({e})") from None
+    for name in _vpa_call.entries():
+        _vpa_call.bind(name, ctypes.cast(getattr(loaded, name), ctypes.c_void_p).value)
+    _call_mod = _vpa_call
+
+
+def call():
+    """The launch entry points (vpa_block_stats ... vpa_greedy_verify_ragged),
+    bound to the loaded libvpa.so: each takes its C arguments in order, a
+    vpa_vocab as three ints and an epilogue as None or (d2t, d2t_len, scale),
+    and returns the vpa_status."""
+    if _lib is None:
+        lib()
+    return _call_mod
 
 
 def last_error() -> str:
@@ -157,8 +187,10 @@ def _stream_arg(fn):
 
 def _on(device, fn, *args):
     """Call the library with `device` current (launches go to the current
-    device), switching only when another device is current."""
-    if device.index is not None and torch.cuda.current_device() != device.index:
+    device), switching only when another device is current.  The caller's
+    tensors live on `device`, so the runtime is initialised and the current
+    device can be read without torch.cuda's initialisation check."""
+    if device.index is not None and torch._C._cuda_getDevice() != device.index:
         with torch.cuda.device(device):
             return fn(*args)
     return fn(*args)
@@ -249,8 +281,8 @@ def block_stats(logits, vocab, shard_width, n_shards, block, rows=None, first_sh
     _same_device(dev, out=out)
     if tuple(out.shape) != (n_local, n_rows, m, 2):
         raise ValueError(f"out has shape {tuple(out.shape)}, expected {(n_local, n_rows, m, 2)}")
-    _check(_on(dev, lib().vpa_block_stats, logits.data_ptr(), _dtype_code(logits), ld,
-               _vocab(vocab, shard_width, n_shards), first_shard, n_local, _vp(rows), n_rows,
+    _check(_on(dev, call().vpa_block_stats, logits.data_ptr(), _dtype_code(logits), ld,
+               vocab, shard_width, n_shards, first_shard, n_local, _vp(rows), n_rows,
                logits.shape[0], block, out.data_ptr(), _stream(stream, dev)))
     return out
 
@@ -287,24 +319,23 @@ def verify_stats(logits, vocab, shard_width, n_shards, n_req, k, block_draft=DRA
         _stats_tensor(dst, "draft_stats")
         _stats_tensor(bst, "bonus_stats")
         _same_device(dev, draft_stats=dst, bonus_stats=bst)
-    _check(_on(dev, lib().vpa_verify_stats, logits.data_ptr(), _dtype_code(logits), ld,
-               _vocab(vocab, shard_width, n_shards), first_shard, n_local, n_req, k, block_draft,
+    _check(_on(dev, call().vpa_verify_stats, logits.data_ptr(), _dtype_code(logits), ld,
+               vocab, shard_width, n_shards, first_shard, n_local, n_req, k, block_draft,
                block_bonus, dst.data_ptr(), bst.data_ptr(), _stream(stream, dev)))
     return dst, bst
 
 
 def _epilogue(d2t, scale, device):
-    """(ctypes Epilogue pointer or None, d2t tensor kept alive)."""
+    """The epilogue argument of a launch: None, or (d2t address, d2t_len, scale)."""
     if d2t is None and scale == 1.0:
-        return None, None
+        return None
     if d2t is not None:
         if d2t.dtype != torch.int64 or not d2t.is_cuda or not d2t.is_contiguous() or d2t.dim() != 1:
             raise ValueError("d2t must be a contiguous 1-D int64 device tensor")
         if d2t.device != device:
             raise ValueError(f"d2t is on {d2t.device}, expected {device}")
-    e = Epilogue(None if d2t is None else d2t.data_ptr(), 0 if d2t is None else d2t.numel(),
-                 float(scale))
-    return ctypes.pointer(e), d2t
+    return (None if d2t is None else d2t.data_ptr(), 0 if d2t is None else d2t.numel(),
+            float(scale))
 
 
 @_stream_arg
@@ -320,8 +351,8 @@ def combine_stats(stats, d2t=None, scale=1.0, *, stream=None):
     buf = torch.empty(2 * n, dtype=torch.int32, device=dev)
     ids, vals = buf.as_strided((n,), (1,), 0), buf.as_strided((n,), (1,), n)
     mapped = torch.empty(n, dtype=torch.int64, device=dev) if d2t is not None else None
-    epi, _keep = _epilogue(d2t, scale, dev)
-    _check(_on(dev, lib().vpa_combine_stats, stats.data_ptr(), s, n, m, epi, ids.data_ptr(),
+    epi = _epilogue(d2t, scale, dev)
+    _check(_on(dev, call().vpa_combine_stats, stats.data_ptr(), s, n, m, epi, ids.data_ptr(),
                vals.data_ptr(), _vp(mapped), _stream(stream, dev)))
     return (ids, vals) if d2t is None else (ids, vals, mapped)
 
@@ -344,7 +375,6 @@ def top_tokens(logits, vocab, shard_width, n_shards, block=DRAFT_BLOCK, workspac
     ld = _logits_ld(logits)
     n = logits.shape[0]
     dev = logits.device
-    voc = _vocab(vocab, shard_width, n_shards)
     if workspace is None and ids is None and val_bits is None:
         # one int32 allocation: the workspace (rounded up to 256 bytes), then
         # ids, then value bits
@@ -371,10 +401,11 @@ def top_tokens(logits, vocab, shard_width, n_shards, block=DRAFT_BLOCK, workspac
     if d2t is not None:
         mapped = (torch.empty(n, dtype=torch.int64, device=dev) if mapped is None
                   else _out_tensor(mapped, "mapped", torch.int64, n, dev))
-    epi, _keep = _epilogue(d2t, scale, dev)
-    _check(_on(dev, lib().vpa_top_tokens, logits.data_ptr(), _dtype_code(logits), ld, voc, n,
-               block, ws_ptr, ws_bytes, epi, ids.data_ptr(), val_bits.data_ptr(),
-               _vp(mapped if d2t is not None else None), _stream(stream, dev)))
+    epi = _epilogue(d2t, scale, dev)
+    _check(_on(dev, call().vpa_top_tokens, logits.data_ptr(), _dtype_code(logits), ld, vocab,
+               shard_width, n_shards, n, block, ws_ptr, ws_bytes, epi, ids.data_ptr(),
+               val_bits.data_ptr(), _vp(mapped if d2t is not None else None),
+               _stream(stream, dev)))
     return (ids, val_bits) if d2t is None else (ids, val_bits, mapped)
 
 
@@ -401,9 +432,9 @@ def top_tokens_noalloc(logits, vocab, shard_width, n_shards, block=DRAFT_BLOCK, 
     if d2t is not None:
         mapped = (torch.empty(n, dtype=torch.int64, device=dev) if mapped is None
                   else _out_tensor(mapped, "mapped", torch.int64, n, dev))
-    epi, _keep = _epilogue(d2t, scale, dev)
-    _check(_on(dev, lib().vpa_top_tokens_noalloc, logits.data_ptr(), _dtype_code(logits), ld,
-               _vocab(vocab, shard_width, n_shards), n, block, epi, ids.data_ptr(),
+    epi = _epilogue(d2t, scale, dev)
+    _check(_on(dev, call().vpa_top_tokens_noalloc, logits.data_ptr(), _dtype_code(logits), ld,
+               vocab, shard_width, n_shards, n, block, epi, ids.data_ptr(),
                val_bits.data_ptr(), _vp(mapped if d2t is not None else None),
                _stream(stream, dev)))
     return (ids, val_bits) if d2t is None else (ids, val_bits, mapped)
@@ -453,7 +484,7 @@ def greedy_verify(draft_stats, bonus_stats, draft_ids, with_targets=True, out=No
                                   or not t.is_contiguous()):
                 raise ValueError("preallocated verification outputs have the wrong shape/dtype")
         _same_device(dev, out_tokens=out_t, num_sampled=ns, num_rejected=nr, target_ids=tg)
-    _check(_on(dev, lib().vpa_greedy_verify, draft_stats.data_ptr(), draft_stats.shape[2],
+    _check(_on(dev, call().vpa_greedy_verify, draft_stats.data_ptr(), draft_stats.shape[2],
                bonus_stats.data_ptr(), bonus_stats.shape[2], s, r, k, draft_ids.data_ptr(),
                _vp(accept), out_t.data_ptr(), ns.data_ptr(), nr.data_ptr(), _vp(tg),
                _stream(stream, dev)))
@@ -476,7 +507,7 @@ def ragged_rows(cu, total_drafts=None, *, stream=None):
     n_req = cu.numel() - 1
     buf = torch.empty(total + n_req, dtype=torch.int32, device=cu.device)
     draft_rows, bonus_rows = buf[:total], buf[total:]
-    _check(_on(cu.device, lib().vpa_ragged_rows, cu.data_ptr(), n_req, total,
+    _check(_on(cu.device, call().vpa_ragged_rows, cu.data_ptr(), n_req, total,
                draft_rows.data_ptr(), bonus_rows.data_ptr(), _stream(stream, cu.device)))
     return draft_rows, bonus_rows
 
@@ -500,8 +531,8 @@ def verify_stats_rows(logits, vocab, shard_width, n_shards, draft_rows, bonus_ro
     buf = torch.empty(nd + n_local * nb_rows * mb * 2, dtype=torch.int32, device=dev)
     dst = buf[:nd].view(n_local, nd_rows, md, 2)
     bst = buf[nd:].view(n_local, nb_rows, mb, 2)
-    _check(_on(dev, lib().vpa_verify_stats_rows, logits.data_ptr(), _dtype_code(logits), ld,
-               _vocab(vocab, shard_width, n_shards), first_shard, n_local, draft_rows.data_ptr(),
+    _check(_on(dev, call().vpa_verify_stats_rows, logits.data_ptr(), _dtype_code(logits), ld,
+               vocab, shard_width, n_shards, first_shard, n_local, draft_rows.data_ptr(),
                nd_rows, bonus_rows.data_ptr(), nb_rows, logits.shape[0], block_draft, block_bonus,
                dst.data_ptr(), bst.data_ptr(), _stream(stream, dev)))
     return dst, bst
@@ -557,7 +588,7 @@ def greedy_verify_ragged(draft_stats, bonus_stats, cu, draft_ids, total_drafts=N
     buf = torch.empty(per * (2 if with_targets else 1) + 2 * n_req, dtype=torch.int32, device=dev)
     out, ns, nr = buf[:per], buf[per:per + n_req], buf[per + n_req:per + 2 * n_req]
     tg = buf[per + 2 * n_req:] if with_targets else None
-    _check(_on(dev, lib().vpa_greedy_verify_ragged, draft_stats.data_ptr(), draft_stats.shape[2],
+    _check(_on(dev, call().vpa_greedy_verify_ragged, draft_stats.data_ptr(), draft_stats.shape[2],
                bonus_stats.data_ptr(), bonus_stats.shape[2], bonus_stats.shape[0], n_req,
                cu.data_ptr(), total, draft_ids.data_ptr(), _vp(prefilling), _vp(accept),
                out.data_ptr(), ns.data_ptr(), nr.data_ptr(), _vp(tg), _stream(stream, dev)))
