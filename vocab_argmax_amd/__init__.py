@@ -113,6 +113,10 @@ def lib():
                                "`python -m vocab_argmax_amd._build` (hipcc, gfx950)")
         loaded = _bind(ctypes.CDLL(LIB_PATH))
         _bind_call(loaded)
+        # sizes cached from a previously loaded library do not carry over
+        stats_slots.cache_clear()
+        top_tokens_workspace.cache_clear()
+        _vocab.cache_clear()
         _lib = loaded
     return _lib
 
