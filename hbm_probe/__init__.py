@@ -2,7 +2,9 @@
 statistics kernel's roofline: a ctypes binding of libvpa_probe.so
 (hbm_probe/vpa_probe.h, built from hbm_probe/read_probe.hip by
 hbm_probe/build.py).  Measurement only: the argmax library neither contains
-nor calls it, and only bench.py and tests/test_read_probe.py load it."""
+nor calls it, and only bench.py and tests/test_read_probe.py load it.
+hbm_probe/block_sizes.py is a separate program for hardware-counter runs:
+it launches the library's statistics kernel with two block sizes."""
 import ctypes
 import os
 
