@@ -194,7 +194,7 @@ def test_top_tokens_d2t_must_cover_vocab(lib):
 def test_top_tokens_rejects(lib):
     voc = V(151936, 76032, 2)
     need = lib.vpa_top_tokens_workspace(voc, 32, 8192)
-    assert need == 2 * 32 * 10 * 8
+    assert need == 32 * 38 * 8            # 38 chunks of 4096 columns per row (chunk_stats.hip)
     assert lib.vpa_top_tokens_workspace(voc, 0, 8192) == 0
     assert lib.vpa_top_tokens_workspace(voc, 32, 0) == 0
     args = dict(ld=152064, n=32, block=8192, ws=FAKE, wsb=need, ids=FAKE)
@@ -403,3 +403,32 @@ def test_module_passes_scale_as_fp32():
     assert "scale" in vpa.last_error()
     args = args[:10] + ((None, 0, 2.0 ** -149),) + args[11:]   # the least fp32 subnormal
     assert c.vpa_top_tokens(*args) == vpa.VPA_OK
+
+
+def test_top_tokens_workspace_covers_both_cuts(lib):
+    """vpa_top_tokens_workspace is the larger of the per-block statistics
+    ([S][n][M]) and, when the sizes allow the chunked statistics of small
+    bf16 batches, the chunk statistics ([n][ceil(V / 4096)])."""
+    ws = lib.vpa_top_tokens_workspace
+    assert ws(V(200064, 25008, 8), 1024, 8192) == 1024 * 49 * 8     # chunks: 49 > 8 * 4
+    assert ws(V(200064, 25008, 8), 1025, 8192) == 1025 * 32 * 8     # past 1024 rows of 200064
+    assert ws(V(200064, 25008, 8), 4096, 8192) == 4096 * 32 * 8
+    assert ws(V(200063, 25008, 8), 64, 8192) == 64 * 32 * 8         # V not a multiple of 8
+    assert ws(V(1000, 125, 8), 32768, 256) == 32768 * 16 * 8        # blocks need more
+    assert ws(V(151936, 76032, 2), 1, 1024) == 2 * 75 * 8           # 1024-blocks need more
+
+
+@pytest.mark.parametrize("dt,base,ld,need", [
+    (vpa.VPA_BF16, FAKE, 152064, 32 * 38 * 8),                         # chunked statistics
+    (vpa.VPA_F32, FAKE, 152064, 2 * 32 * 10 * 8),                      # fp32: per-block
+    (vpa.VPA_BF16, ctypes.c_void_p(0x7F0000010008), 152064, 2 * 32 * 10 * 8),   # not 16-aligned
+    (vpa.VPA_BF16, FAKE, 152068, 2 * 32 * 10 * 8),                     # ld not a multiple of 8
+])
+def test_top_tokens_picks_its_statistics_cut(lib, dt, base, ld, need):
+    """Which statistics a call takes shows in the workspace bytes it asks for
+    (every call here is rejected before anything is enqueued)."""
+    voc = V(151936, 76032, 2)
+    st = lib.vpa_top_tokens(base, dt, ld, voc, 32, 8192, FAKE, need - 8, None, FAKE, None, None,
+                            None)
+    assert st == vpa.VPA_ERR_INVALID
+    assert f"smaller than {need} bytes" in vpa.last_error()

@@ -1,5 +1,6 @@
-"""A CPU model of the statistics kernel's index arithmetic
-(vocab_argmax_amd/csrc/block_stats.hip), checked over random geometries:
+"""A CPU model of the statistics kernels' index arithmetic
+(vocab_argmax_amd/csrc/block_stats.hip, and chunk_stats.hip further down),
+checked over random geometries:
 
 - the item decode covers every (row, shard, slot) of a launch exactly once
   and every statistic index lies inside [0, n_local * n_rows * M);
@@ -159,12 +160,95 @@ def test_statistics_kernel_index_arithmetic(esize):
     assert segments > 1000
 
 
+def _source(name):
+    import os
+    return open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                             "vocab_argmax_amd", "csrc", name)).read()
+
+
 def test_model_matches_the_kernel_constants():
     """The constants the model assumes are the ones the kernel source sets."""
-    import os
-    src = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                            "vocab_argmax_amd", "csrc", "block_stats.hip")).read()
+    src = _source("block_stats.hip")
     assert "#define VPA_LANE_ITERS 16" in src
     assert "#define VPA_PIPE_BF16 8" in src
     assert "#define VPA_PIPE_F32 16" in src
-    assert "i = i < ilast ? i : ilast;" in src            # clamped chunk indices
+    assert "i = i < ilast ? i : ilast;" in _source("vpa_scan.h")   # clamped chunk indices
+
+
+# The chunked statistics of vpa_top_tokens (chunk_stats.hip) for bf16
+# batches of up to CHUNK_MAX_BYTES: chunk c of the flattened (row, chunk)
+# space is columns [q*CHUNK_COLS, min((q+1)*CHUNK_COLS, V)) of row c // Q,
+# Q = ceil(V / CHUNK_COLS), read by wavefront c mod W; its statistic goes to
+# stats[c].  The host takes this path only for V and ld multiples of 8 and a
+# 16-byte aligned base (api.hip, chunk_sizes).
+CHUNK_LOADS = 8                         # kChunkLoads
+CHUNK_COLS = 64 * 8 * CHUNK_LOADS       # kChunkCols
+CHUNK_MAX_BYTES = 1024 * 200064 * 2     # kChunkMaxBytes
+GROUPS_PER_CU = 2                       # kGroupsPerCU
+
+
+def chunk_sizes(vocab, ld, n_rows):
+    return vocab % 8 == 0 and ld % 8 == 0 and 0 < n_rows <= CHUNK_MAX_BYTES // (2 * vocab)
+
+
+def check_chunk_launch(rng):
+    vocab = 8 * rng.choice([1, 2, 3, rng.randint(1, 600), rng.randint(500, 40000), 25008])
+    ld = vocab + 8 * rng.choice([0, 0, 1, rng.randint(0, 300)])
+    n_rows = rng.randint(1, min(CHUNK_MAX_BYTES // (2 * vocab), 40))
+    assert chunk_sizes(vocab, ld, n_rows)
+    per_row = -(-vocab // CHUNK_COLS)
+    n_chunks = n_rows * per_row
+    cus = rng.choice([1, 3, 80, 256, 304])
+    groups = min(GROUPS_PER_CU * cus, -(-n_chunks // 4))
+    n_waves = groups * 4
+    visited = [0] * n_chunks
+    spans = {}                                            # row -> [(lo, hi)]
+    for wave in range(n_waves):
+        for c in range(wave, n_chunks, n_waves):
+            visited[c] += 1
+            row = c // per_row
+            col0 = (c - row * per_row) * CHUNK_COLS
+            cols = min(vocab - col0, CHUNK_COLS)
+            nv = cols // 8
+            assert 0 <= row < n_rows and cols > 0 and cols % 8 == 0 and nv >= 1
+            assert col0 % 8 == 0 and (row * ld + col0) % 8 == 0       # 16-byte aligned vectors
+            # the loads: lane l, vector u reads vector min(l + 64u, nv - 1)
+            last = max(min(lane + 64 * u, nv - 1) for lane in (0, 63) for u in (0, CHUNK_LOADS - 1))
+            assert last == min(63 + 64 * (CHUNK_LOADS - 1), nv - 1)
+            assert row * ld + col0 + last * 8 + 7 < row * ld + vocab   # valid columns only
+            # fold decode of the last element a lane can pack (u = 7, e = 7)
+            for lane in (0, 17, 63):
+                pos = (CHUNK_LOADS - 1) * 8 + 7
+                i = min(lane + 64 * (pos >> 3), nv - 1)
+                assert col0 + i * 8 + (pos & 7) < vocab
+            spans.setdefault(row, []).append((col0, col0 + nv * 8))
+    assert visited == [1] * n_chunks                      # every statistic written once
+    for row in range(n_rows):                             # the chunks tile [0, V) exactly
+        got = sorted(spans[row])
+        assert got[0][0] == 0 and got[-1][1] == vocab
+        assert all(a[1] == b[0] for a, b in zip(got, got[1:]))
+    return n_chunks
+
+
+def test_chunk_statistics_index_arithmetic():
+    rng = random.Random(2002)
+    chunks = sum(check_chunk_launch(rng) for _ in range(120))
+    assert chunks > 2000
+
+
+def test_chunk_statistics_counts_fit_int32():
+    """The largest eligible batch of any vocabulary stays far below 2^31
+    chunks (the kernel and the combine index them with int32)."""
+    for vocab in [8 * k for k in (1, 2, 7, 100, 512, 513, 25008, 2 ** 21 - 1)]:
+        n_rows = CHUNK_MAX_BYTES // (2 * vocab)
+        assert n_rows * -(-vocab // CHUNK_COLS) < 2 ** 31 // 8
+
+
+def test_chunk_model_matches_the_kernel_constants():
+    src = _source("chunk_stats.hip")
+    assert "constexpr int kChunkLoads = 8;" in src
+    assert "constexpr int kChunkCols = 64 * 8 * kChunkLoads;" in src
+    assert "constexpr int kGroupsPerCU = 2;" in src
+    assert "k.row = c / per_row;" in src and "k.col0 = (c - k.row * per_row) * kChunkCols;" in src
+    assert "constexpr int64_t kChunkMaxBytes = (int64_t)1024 * 200064 * 2;" in _source("api.hip")
+    assert "return v.vocab % 8 == 0 && ld % 8 == 0 && n_rows > 0 &&" in _source("api.hip")

@@ -882,6 +882,82 @@ def test_hip_graph_replays_match_eager():
             assert_same(a, b, f"graph replay {rep} vs oracle")
 
 
+def _chunk_case(n, vocab, ld, seed):
+    """bf16 rows with planted maxima where the chunked statistics of
+    vpa_top_tokens (4096-column chunks) could go wrong; padding columns
+    [vocab, ld) hold +inf and NaN, which must never be read."""
+    g = torch.Generator().manual_seed(seed)
+    x = (torch.randn((n, ld), generator=g) * 3).to(torch.bfloat16)
+    x[:, vocab:] = float("inf")
+    if ld > vocab + 1:
+        x[:, vocab + 1] = float("nan")
+    big = 1e4
+    plants = [
+        [(0, big)],                                          # first column
+        [(vocab - 1, big)],                                  # last column
+        [(4095, big), (4096, big)],                          # tie across a chunk edge
+        [(vocab - 1, big), (max(vocab - 4097, 0), big)],     # tie, the lower id in another chunk
+        [(min(5000, vocab - 1), None), (vocab - 1, None)],   # NaNs: the first wins
+        "neg_inf",                                           # every column -inf
+        "signed_zeros",                                      # -0 everywhere, +0 later: keys tie
+        [(min(8191, vocab - 1), float("inf")), (min(8192, vocab - 1), float("inf"))],
+    ]
+    for r, plant in enumerate(plants[:n]):
+        if plant == "neg_inf":
+            x[r, :vocab] = float("-inf")
+        elif plant == "signed_zeros":
+            x[r, :vocab] = -0.0
+            x[r, min(7000, vocab - 1)] = 0.0
+        else:
+            for col, val in plant:
+                col = min(col, vocab - 1)
+                if val is None:   # a NaN with a payload of its own
+                    x[r, col] = torch.tensor([0x7FC1 + col % 7], dtype=torch.int16).view(torch.bfloat16)
+                else:
+                    x[r, col] = val
+    return x
+
+
+@pytest.mark.parametrize("n,vocab,ld", [
+    (64, 200064, 200064),           # the argmax workload's vocabulary
+    (1024, 200064, 200064),         # its 1024-row batch, the largest chunked one at this width
+    (37, 4096 * 3 + 8, 4096 * 3 + 32),  # a short last chunk, padding columns
+    (9, 8, 16),                     # one vector per row
+    (300, 4096, 4096),              # exactly one chunk per row
+    (12, (1 << 24) - 8, (1 << 24) - 8),  # the largest vocabulary, 4096 chunks per row
+])
+def test_top_tokens_chunked_statistics(n, vocab, ld):
+    """Small bf16 batches take their top_tokens statistics from the chunked
+    launch.  Its ids and value bits, with and without the epilogue, equal the
+    oracle's, and equal the per-block launch's on the same data (a view
+    offset by one element is not 16-byte aligned, so it takes that path)."""
+    assert vocab % 8 == 0 and ld % 8 == 0 and n * vocab * 2 <= 1024 * 200064 * 2
+    x_cpu = _chunk_case(n, vocab, ld, seed=n + vocab)
+    want_ids, want_vals = oracle.argmax(x_cpu[:, :vocab].contiguous(), vocab)
+    x = _dev(x_cpu)
+    s = 2
+    w = -(-vocab // s)
+    _announce(f"chunked top_tokens {n} x {vocab} (ld {ld})")
+    ids, vals = vpa.top_tokens(x, vocab, w, s)
+    assert_same(ids, want_ids, "chunked ids")
+    assert_same(vals.to(torch.int64) & 0xFFFFFFFF, want_vals, "chunked value bits")
+    shifted = torch.empty((n, ld + 8), dtype=torch.bfloat16, device=DEV)
+    xv = shifted[:, 1:1 + ld]
+    xv.copy_(x)
+    assert xv.data_ptr() % 16 != 0
+    ids2, vals2 = vpa.top_tokens(xv, vocab, w, s)
+    assert_same(ids2, want_ids, "per-block ids on the same data")
+    assert_same(vals2.to(torch.int64) & 0xFFFFFFFF, want_vals, "per-block value bits")
+    # the epilogue after chunked statistics
+    g = torch.Generator().manual_seed(7)
+    d2t = torch.randint(0, 1000, (vocab,), generator=g, dtype=torch.int64)
+    ids3, vals3, mapped = vpa.top_tokens(x, vocab, w, s, d2t=_dev(d2t), scale=1 / 0.7)
+    assert_same(ids3, want_ids, "chunked ids with the epilogue")
+    assert_same(mapped, oracle.map_ids(want_ids, d2t), "chunked mapped ids")
+    assert_same(vals3.to(torch.int64) & 0xFFFFFFFF,
+                oracle.scale_bits(want_vals, 1 / 0.7), "chunked scaled maxima")
+
+
 def test_empty_batch_gpu():
     x = torch.empty((0, 1000), dtype=torch.bfloat16, device=DEV)
     st = vpa.block_stats(x, 1000, 125, 8, 256)

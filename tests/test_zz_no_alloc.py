@@ -74,10 +74,11 @@ def test_noalloc_matches_top_tokens_on_consecutive_calls():
 
 
 def test_noalloc_at_its_size_limit():
-    """V = 1000 over 8 shards of 125 with 256-blocks: 16 statistics (128 B)
-    per row, so 32768 rows fill the 4 MiB array exactly; one more row is
+    """V = 1001 over 8 shards of 126 with 256-blocks: 16 statistics (128 B)
+    per row (V is not a multiple of 8, so these are the per-block
+    statistics), so 32768 rows fill the 4 MiB array exactly; one more row is
     refused with nothing enqueued."""
-    v, wd, s, b = 1000, 125, 8, 256
+    v, wd, s, b = 1001, 126, 8, 256
     per_row = vpa.top_tokens_workspace(v, wd, s, 1, b)
     n = vpa.NOALLOC_WORKSPACE_BYTES // per_row
     assert n * per_row == vpa.NOALLOC_WORKSPACE_BYTES and n == 32768

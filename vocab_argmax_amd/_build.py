@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libvpa.so")
-SOURCES = ["api.hip", "block_stats.hip", "reduce.hip"]
+SOURCES = ["api.hip", "block_stats.hip", "chunk_stats.hip", "reduce.hip"]
 ARCH = "gfx950"
 PYCALL = os.path.join(PKG, "_vpa_call" + sysconfig.get_config_var("EXT_SUFFIX"))
 

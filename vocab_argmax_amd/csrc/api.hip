@@ -192,16 +192,35 @@ vpa_status set_items(vpa::SegTask& t, int64_t n_rows, const char* what) {
     return ok();
 }
 
+// Batches of bf16 logits up to this size (1024 rows of a 200064-entry
+// vocabulary) take their vpa_top_tokens statistics from the chunked launch
+// (chunk_stats.hip); larger ones from the per-block launch, which streams
+// faster once the batch is large enough to amortise its longer drain.  On
+// MI355X the chunked launch measured 0.5-4.7 % faster from 96 to 1024 rows
+// of 200064 and slower from 1152.
+constexpr int64_t kChunkMaxBytes = (int64_t)1024 * 200064 * 2;
+
+// Whether vpa_top_tokens' statistics of these logits may come from the
+// chunked launch, as far as the sizes tell (dtype and alignment aside).
+bool chunk_sizes(const vpa_vocab& v, int64_t ld, int64_t n_rows) {
+    return v.vocab % 8 == 0 && ld % 8 == 0 && n_rows > 0 &&
+           n_rows <= kChunkMaxBytes / (2 * v.vocab);
+}
+
 // A validated vpa_top_tokens call: the statistics task over all S shards of
-// every row ([S][n_rows][M], as vpa_block_stats cuts them), the workspace
+// every row ([S][n_rows][M], as vpa_block_stats cuts them), or, for small
+// bf16 batches, the chunked statistics ([n_rows][chunk_m]); the workspace
 // bytes it needs, and the resolved epilogue.  (Cutting each row at global
-// block edges only, ignoring shard edges, and cutting the launch's last rows
-// into smaller blocks were both measured; neither was faster.)
+// block edges only, ignoring shard edges, cutting the launch's last rows
+// into smaller blocks and cutting each shard into equal parts were
+// measured for the per-block launch; none was faster.)
 struct TopCall {
     vpa::SegTask task;
     size_t ws_bytes;
     Epi epi;
     int esize;
+    bool chunks;
+    int32_t chunk_m;
 };
 
 vpa_status check_top_tokens(const void* logits, int dtype, int64_t ld, const vpa_vocab& v,
@@ -227,6 +246,10 @@ vpa_status check_top_tokens(const void* logits, int dtype, int64_t ld, const vpa
     c.esize = esize_of(dtype);
     c.task.base = (const unsigned char*)logits;
     c.task.logits_rows = n_rows;
+    c.chunks = dtype == VPA_BF16 && aligned(logits, 16) && chunk_sizes(v, ld, n_rows);
+    c.chunk_m = c.chunks ? vpa::chunk_stats_per_row(v.vocab) : 0;
+    if (c.chunks)
+        c.ws_bytes = (size_t)n_rows * (size_t)c.chunk_m * sizeof(vpa_stat);
     vpa::SegTask none{};
     if ((st = check_dispatch(vpa::block_stats_threads(c.esize, c.task, none),
                              "vpa_top_tokens (statistics)")) != VPA_OK ||
@@ -241,11 +264,18 @@ vpa_status launch_top_tokens(TopCall& c, vpa_stat* ws, int32_t* ids, uint32_t* v
                              int64_t* mapped, hipStream_t stream) {
     c.task.stats = ws;
     vpa::SegTask none{};
-    hipError_t e = vpa::launch_block_stats(c.esize, c.task, none, stream);
+    hipError_t e = c.chunks ? vpa::launch_chunk_stats(c.task.base, c.task.ld,
+                                                      (int32_t)c.task.vocab, c.task.n_rows, ws,
+                                                      stream)
+                            : vpa::launch_block_stats(c.esize, c.task, none, stream);
     if (e != hipSuccess)
         return hip_fail(e, "vpa_top_tokens statistics launch");
-    e = vpa::launch_combine(ws, c.task.n_local, c.task.n_rows, c.task.m, c.epi.d2t, c.epi.d2t_len,
-                            c.epi.scale, ids, val_bits, mapped, stream);
+    if (c.chunks)
+        e = vpa::launch_combine(ws, 1, c.task.n_rows, c.chunk_m, c.epi.d2t, c.epi.d2t_len,
+                                c.epi.scale, ids, val_bits, mapped, stream);
+    else
+        e = vpa::launch_combine(ws, c.task.n_local, c.task.n_rows, c.task.m, c.epi.d2t,
+                                c.epi.d2t_len, c.epi.scale, ids, val_bits, mapped, stream);
     return e == hipSuccess ? ok() : hip_fail(e, "vpa_top_tokens combine launch");
 }
 
@@ -463,7 +493,15 @@ size_t vpa_top_tokens_workspace(vpa_vocab v, int64_t n_rows, int32_t block) {
     const int64_t per_row = (int64_t)v.n_shards * m;
     if (per_row > INT32_MAX || n_rows > INT32_MAX / per_row)
         return 0;
-    return (size_t)(per_row * n_rows) * sizeof(vpa_stat);
+    size_t need = (size_t)(per_row * n_rows) * sizeof(vpa_stat);
+    // The row stride and the dtype are not known here: whenever the sizes
+    // allow the chunked statistics, the workspace covers them too.
+    if (chunk_sizes(v, v.vocab, n_rows)) {
+        const size_t chunks = (size_t)n_rows * (size_t)vpa::chunk_stats_per_row(v.vocab) *
+                              sizeof(vpa_stat);
+        need = chunks > need ? chunks : need;
+    }
+    return need;
 }
 
 vpa_status vpa_top_tokens(const void* logits, vpa_dtype dtype, int64_t ld, vpa_vocab v,

@@ -52,6 +52,14 @@ struct SegTask {
     int32_t n_waves;            // wavefronts this task occupies (set by launch_block_stats)
 };
 
+// Statistics of vpa_top_tokens for small bf16 batches (chunk_stats.hip): one
+// statistic per chunk of chunk_stats_per_row(V) columns of a row, laid out
+// [rows][chunk_stats_per_row(V)].  The logits must be bf16 with V and ld
+// multiples of 8 and a 16-byte aligned base.
+int32_t chunk_stats_per_row(int64_t vocab);
+hipError_t launch_chunk_stats(const void* logits, int64_t ld, int32_t vocab, int32_t n_rows,
+                              vpa_stat* stats, hipStream_t stream);
+
 // Launch the block-statistics kernel over the items of t0 followed by those
 // of t1 (t1.n_items may be 0).  Both tasks share dtype `esize` (2 or 4).
 hipError_t launch_block_stats(int esize, const SegTask& t0, const SegTask& t1, hipStream_t stream);
