@@ -54,7 +54,8 @@ B_DRAFT, B_BONUS = 8192, 1024
 F32_ROWS = 1024                             # fp32 leg: 2 x 1024 x 200064 x 4 B = 1.6 GB
 REPEATS = 5                                 # per-call timings: median of 5 windows
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "block_stats_bf16_v200064_traffic.json")
-KERNEL_SOURCES = ("vocab_argmax_amd/csrc/block_stats.hip", "vocab_argmax_amd/csrc/vpa_device.h")
+KERNEL_SOURCES = ("vocab_argmax_amd/csrc/block_stats.hip", "vocab_argmax_amd/csrc/vpa_scan.h",
+                  "vocab_argmax_amd/csrc/vpa_device.h")
 
 
 def slots(w, s, b):

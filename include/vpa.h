@@ -196,13 +196,22 @@ vpa_status vpa_combine_stats(const vpa_stat* stats, int32_t n_shards, int64_t n_
                              int64_t* mapped, void* stream);
 
 /* Workspace bytes vpa_top_tokens needs for n_rows rows (0 if the arguments
- * are invalid or n_rows is 0). */
+ * are invalid or n_rows is 0): enough for either cut of its statistics (see
+ * vpa_top_tokens), whatever the dtype and row stride of the call. */
 size_t vpa_top_tokens_workspace(vpa_vocab v, int64_t n_rows, int32_t block);
 
 /* Fused draft-side get_top_tokens over every shard of a row (PR #62604,
- * "Purpose" item 2): padding mask, per-block statistics of all S shards in
- * rank order (kept in `workspace`, [S][n_rows][M]), and their combination
- * into the global argmax.
+ * "Purpose" item 2): padding mask, statistics of every row kept in
+ * `workspace`, and their combination into the global argmax.  The ids and
+ * maxima do not depend on how a row is cut into statistics, so the library
+ * picks the cut:
+ *  - bf16 batches of at most 409,731,072 bytes of valid columns (1024 rows
+ *    of a 200064-entry vocabulary), with V and ld multiples of 8 and a
+ *    16-byte aligned logits pointer: one statistic per 4096-column chunk of
+ *    a row, from a persistent launch that sweeps the batch;
+ *  - otherwise the per-block statistics of all S shards in rank order,
+ *    [S][n_rows][M] with the given block size, as vpa_block_stats cuts them.
+ *  The workspace's layout is therefore internal.
  *  logits     [n_rows, ld] holding all S shards side by side (global column
  *             c at logits[row*ld + c]); ld >= V.
  *  workspace  device memory of at least vpa_top_tokens_workspace() bytes,
